@@ -1,0 +1,14 @@
+"""MoE expert operation of a speculative-decoding verification pass on MI355X.
+
+Per-slot and deduplicating expert kernels (hand-written HIP for gfx950) behind the
+C ABI of ``include/moe_expert.h``, plus the host byte accounting and step-time
+model.  This package is the thin Python binding; it fails loudly when the native
+library is missing.
+"""
+from ._abi import (  # noqa: F401
+    MOE_KIND_DEDUP, MOE_KIND_SLOT, MoeError, lib,
+)
+from .ops import (  # noqa: F401
+    Grouping, Layer, bytes_requested, expert_dedup, expert_perslot, kernels_per_call, route_group,
+    step_time_model,
+)

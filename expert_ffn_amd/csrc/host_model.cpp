@@ -1,0 +1,160 @@
+// Host-side byte accounting and step-time model (double precision).
+//
+// Lan, arXiv:2610.34440:
+//   Section 1 "Bytes":  per-slot requests n m w, deduplicating requests X(n) w.
+//   Section 1 "Speculative decoding", Section 3.1 Eq. (5)-(6), Section 3.2
+//   Eqs. (8)-(9), Section 3.3 and Appendix B.3 (staircase, step points (B.31),
+//   convex case (B.36)), Section 3.4 Eqs. (14) and (16).
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "moe_expert.h"
+
+namespace {
+
+double geo(double a, int k) {  // G_a(k) = 1 + a + ... + a^k, summed from the top for accuracy
+    double g = 0.0;
+    for (int i = k; i >= 0; --i) g = g * a + 1.0;
+    return g;
+}
+
+// T_a(k) > T_a(i)  <=>  G_a(k) V(i) > G_a(i) V(k)   (V > 0)
+bool beats(double a, int k, int i, const double* V) { return geo(a, k) * V[i] > geo(a, i) * V[k]; }
+
+// alpha_{k,i} = inf{a in [0,1) : T_a(k) > T_a(i)}, 1 if empty.  The set is upward
+// closed (Appendix B.3, (B.26)-(B.27)), so bisection applies.
+double alpha(int k, int i, const double* V) {
+    if (beats(0.0, k, i, V)) return 0.0;
+    const double near1 = nextafter(1.0, 0.0);
+    if (!beats(near1, k, i, V)) return 1.0;
+    double lo = 0.0, hi = near1;
+    for (int it = 0; it < 200 && hi - lo > 0.0; ++it) {
+        const double mid = 0.5 * (lo + hi);
+        if (mid <= lo || mid >= hi) break;
+        if (beats(mid, k, i, V)) hi = mid;
+        else lo = mid;
+    }
+    return hi;
+}
+
+int kstar(double a, const double* V, int K) {
+    int best = 0;
+    for (int k = 1; k <= K; ++k)
+        if (geo(a, k) * V[best] > geo(a, best) * V[k]) best = k;
+    return best;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t bytes_requested(int32_t kind, const moe_layer_desc* d, const int32_t* ids, int32_t n) {
+    if (!d || !ids) return -(int64_t)(-MOE_E_INVAL);
+    if (kind != MOE_KIND_SLOT && kind != MOE_KIND_DEDUP) return -(int64_t)(-MOE_E_INVAL);
+    if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return -(int64_t)(-MOE_E_DTYPE);
+    if (d->N < 1 || d->N > MOE_MAX_EXPERTS || d->m < 1 || d->m > d->N || n < 1 || d->d_model < 1 || d->d_ff < 1)
+        return -(int64_t)(-MOE_E_INVAL);
+    const int64_t esize = d->dtype == MOE_BF16 ? 2 : 4;
+    const int64_t w = 3 * (int64_t)d->d_model * d->d_ff * esize;
+    const int m = d->m;
+    std::vector<char> seen((size_t)d->N, 0);
+    int64_t U = 0;
+    for (int64_t s = 0; s < (int64_t)n * m; ++s) {
+        const int32_t e = ids[s];
+        if (e < 0 || e >= d->N) return -(int64_t)(-MOE_E_IDS);
+        const int64_t t = s / m, j = s % m;
+        for (int64_t jj = 0; jj < j; ++jj)
+            if (ids[t * m + jj] == e) return -(int64_t)(-MOE_E_IDS);
+        if (!seen[e]) {
+            seen[e] = 1;
+            ++U;
+        }
+    }
+    return kind == MOE_KIND_SLOT ? (int64_t)n * m * w : U * w;
+}
+
+int step_time_model(const moe_step_in* in, moe_step_out* out) {
+    if (!in || !out) return MOE_E_INVAL;
+    const int NM = in->n_max;
+    if (NM < 2 || NM > MOE_STEP_NMAX || in->n_a < 1 || in->n_a > MOE_STEP_AMAX) return MOE_E_INVAL;
+    if (!(in->m_W > 0.0) || !(in->beta_D > 0.0)) return MOE_E_INVAL;
+    for (int p = 0; p < 2; ++p)
+        for (int i = 0; i < NM; ++i)
+            if (!(in->beta[p][i] > 0.0)) return MOE_E_INVAL;
+    for (int i = 0; i < in->n_a; ++i)
+        if (!(in->a[i] >= 0.0 && in->a[i] <= 1.0)) return MOE_E_INVAL;
+    memset(out, 0, sizeof(*out));
+    const int K = NM - 1;  // k_max
+
+    for (int p = 0; p < 2; ++p)
+        for (int n = 1; n <= NM; ++n)
+            out->tau[p][n - 1] = in->t0 + (in->D + in->kv[n - 1]) / in->beta_D +
+                                 in->E[p][n - 1] / in->beta[p][n - 1] + in->phi[p][n - 1];
+    for (int n = 1; n <= NM; ++n) out->S[n - 1] = out->tau[0][n - 1] - out->tau[1][n - 1];
+    out->crossover = 0;
+    for (int n = NM; n >= 2; --n) {
+        if (out->S[n - 1] > 0.0) out->crossover = n;
+        else break;
+    }
+
+    for (int p = 0; p < 2; ++p) {
+        double* V = out->V[p];
+        V[0] = out->tau[0][0] + in->h[0];  // a one-token pass runs the same kernel either way
+        for (int k = 1; k <= K; ++k) V[k] = out->tau[p][k] + in->h[k];
+        bool pos = true;
+        for (int k = 0; k <= K; ++k) pos = pos && V[k] > 0.0;
+        if (!pos) return MOE_E_INVAL;
+        out->a0[p] = V[1] / V[0] - 1.0;
+        for (int ia = 0; ia < in->n_a; ++ia) {
+            const double a = in->a[ia];
+            const int ks = kstar(a, V, K);
+            out->kstar[p][ia] = ks;
+            out->speedup[p][ia] = geo(a, ks) * V[0] / V[ks];
+        }
+        for (int j = 1; j <= K; ++j) {
+            double mx = 0.0;
+            for (int i = 0; i < j; ++i) {
+                double mn = 1.0;
+                for (int k = j; k <= K; ++k) {
+                    const double al = alpha(k, i, V);
+                    if (al < mn) mn = al;
+                }
+                if (mn > mx) mx = mn;
+            }
+            out->step_point[p][j] = mx;
+        }
+        bool convex = true;
+        double cprev = -1.0;
+        for (int k = 1; k <= K; ++k) {
+            const double c = V[k] - V[k - 1];
+            if (c < 0.0 || (k > 1 && c < cprev)) convex = false;
+            cprev = c;
+        }
+        out->convex[p] = convex ? 1 : 0;
+        const double a1 = (V[1] - V[0]) / V[0];
+        out->a1_convex[p] = a1 < 1.0 ? a1 : 1.0;
+    }
+
+    const double mW = in->m_W;
+    const double tau1 = out->tau[0][0];
+    const double beta1 = in->beta[0][0];
+    for (int ia = 0; ia < in->n_a; ++ia) {
+        const double a = in->a[ia];
+        for (int k = 1; k <= K; ++k) {
+            const double Gm1 = geo(a, k) - 1.0;
+            const double Bk = in->beta[1][k];
+            const double dD = in->kv[k] - in->kv[0];
+            const double dphi = in->phi[1][k] - in->phi[0][0];
+            const double bracket = Gm1 * tau1 - dD / in->beta_D - dphi;
+            out->rho_star[ia][k] = 1.0 - Bk / (mW * k) * bracket - (Bk / beta1 - 1.0) / k;
+            const double V0b = in->D + mW + in->kv[0];
+            out->rho_star_bytes[ia][k] = 1.0 - (Gm1 * V0b - dD) / (mW * k);
+        }
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"

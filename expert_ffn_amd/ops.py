@@ -1,0 +1,189 @@
+"""PyTorch-facing binding of the C ABI: argument marshalling only.
+
+PyTorch supplies device memory and the stream; every step of the expert
+operation runs in the library's HIP kernels.
+"""
+import ctypes
+from collections import namedtuple
+
+import numpy as np
+import torch
+
+from . import _abi
+from ._abi import MOE_BF16, MOE_F32, MOE_KIND_DEDUP, MOE_KIND_SLOT, check, lib
+
+Grouping = namedtuple("Grouping", ["count", "offset", "slot_by_expert", "distinct", "u_and_err"])
+
+
+def _vp(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError("weights and x must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _check_dev(name, t, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+class Layer:
+    """Device weights of one MoE layer: W_gate, W_up [N][d_ff][d], W_down [N][d][d_ff]."""
+
+    def __init__(self, w_gate, w_up, w_down, m):
+        N, d_ff, d = w_gate.shape
+        _check_dev("w_gate", w_gate)
+        _check_dev("w_up", w_up, w_gate.dtype, (N, d_ff, d))
+        _check_dev("w_down", w_down, w_gate.dtype, (N, d, d_ff))
+        self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
+        self.N, self.m, self.d, self.d_ff = N, int(m), d, d_ff
+        self.dtype = w_gate.dtype
+        self._weights = _abi.LayerWeights(w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr())
+
+    def desc(self, accumulate=False):
+        return _abi.LayerDesc(self.N, self.m, self.d, self.d_ff, _dtype_code(self.w_gate),
+                              _abi.MOE_FLAG_ACCUMULATE if accumulate else 0)
+
+    @property
+    def expert_bytes(self):
+        return 3 * self.d * self.d_ff * self.w_gate.element_size()
+
+    def workspace(self, n, kind=MOE_KIND_SLOT):
+        nb = lib().moe_workspace_bytes(ctypes.byref(self.desc()), int(n), int(kind))
+        if nb == 0:
+            raise _abi.MoeError("moe_workspace_bytes", _abi.MOE_E_INVAL)
+        return torch.empty(nb, dtype=torch.uint8, device=self.w_gate.device)
+
+
+def route_group(ids, N, out=None, stream=None):
+    """Group the pass's slots by expert (one kernel launch)."""
+    _check_dev("ids", ids, torch.int32)
+    n, m = ids.shape
+    dev = ids.device
+    if out is None:
+        out = Grouping(torch.empty(N, dtype=torch.int32, device=dev), torch.empty(N + 1, dtype=torch.int32, device=dev),
+                       torch.empty(n * m, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.int32, device=dev),
+                       torch.empty(2, dtype=torch.int32, device=dev))
+    st = lib().moe_route_group(_vp(ids), n, m, N, _vp(out.count), _vp(out.offset), _vp(out.slot_by_expert),
+                               _vp(out.distinct), _vp(out.u_and_err), _stream(stream))
+    check("moe_route_group", st)
+    return out
+
+
+def _prep(layer, x, ids, w, y, ws, kind):
+    n = x.shape[0]
+    _check_dev("x", x, layer.dtype, (n, layer.d))
+    _check_dev("ids", ids, torch.int32, (n, layer.m))
+    _check_dev("w", w, torch.float32, (n, layer.m))
+    if y is None:
+        y = torch.empty(n, layer.d, dtype=torch.float32, device=x.device)
+    _check_dev("y", y, torch.float32, (n, layer.d))
+    if ws is None:
+        ws = layer.workspace(n, kind)
+    return n, y, ws
+
+
+def _events(events):
+    if events is None:
+        return ctypes.c_void_p(0), 0
+    arr = (ctypes.c_void_p * len(events))(*[e for e in events])
+    return arr, len(events)
+
+
+def expert_perslot(layer, x, ids, w, y=None, ws=None, accumulate=False, stream=None, events=None):
+    """The expert operation by the per-slot kernel; returns y [n][d] fp32."""
+    n, y, ws = _prep(layer, x, ids, w, y, ws, MOE_KIND_SLOT)
+    desc = layer.desc(accumulate)
+    if events is None:
+        st = lib().moe_expert_perslot(ctypes.byref(desc), ctypes.byref(layer._weights), _vp(x), _vp(ids), _vp(w), n,
+                                      _vp(y), _vp(ws), ws.numel(), _stream(stream))
+    else:
+        ev, nev = _events(events)
+        st = lib().moe_expert_perslot_ev(ctypes.byref(desc), ctypes.byref(layer._weights), _vp(x), _vp(ids), _vp(w),
+                                         n, _vp(y), _vp(ws), ws.numel(), _stream(stream), ev, nev)
+    check("moe_expert_perslot", st)
+    return y
+
+
+def expert_dedup(layer, x, ids, w, grouping, y=None, ws=None, accumulate=False, stream=None, events=None):
+    """The expert operation by the deduplicating kernel, given route_group's
+    output for the same ids; returns y [n][d] fp32."""
+    n, y, ws = _prep(layer, x, ids, w, y, ws, MOE_KIND_DEDUP)
+    g = grouping
+    desc = layer.desc(accumulate)
+    args = [ctypes.byref(desc), ctypes.byref(layer._weights), _vp(x), _vp(ids), _vp(w), n, _vp(g.offset),
+            _vp(g.slot_by_expert), _vp(g.distinct), _vp(g.u_and_err), _vp(y), _vp(ws), ws.numel(), _stream(stream)]
+    if events is None:
+        st = lib().moe_expert_dedup(*args)
+    else:
+        ev, nev = _events(events)
+        st = lib().moe_expert_dedup_ev(*args, ev, nev)
+    check("moe_expert_dedup", st)
+    return y
+
+
+def kernels_per_call(kind):
+    return lib().moe_kernels_per_call(int(kind))
+
+
+def bytes_requested(kind, N, m, d, d_ff, dtype, ids_host):
+    """Expert bytes requested by kernel ``kind`` for host ids [n][m]."""
+    ids_host = np.ascontiguousarray(ids_host, dtype=np.int32)
+    n = ids_host.shape[0]
+    code = MOE_BF16 if dtype in ("bf16", torch.bfloat16) else MOE_F32
+    desc = _abi.LayerDesc(N, m, d, d_ff, code, 0)
+    v = lib().bytes_requested(int(kind), ctypes.byref(desc), ids_host.ctypes.data_as(ctypes.c_void_p), n)
+    if v < 0:
+        raise _abi.MoeError("bytes_requested", int(v))
+    return int(v)
+
+
+def step_time_model(n_max, a, m_W, E, beta, t0=0.0, D=0.0, kv=None, beta_D=1.0, phi=None, h=None):
+    """Evaluate the step-time model.  E, beta, phi: [2][n_max] (kind, n-1); kv, h:
+    [n_max] (k).  Returns a dict of numpy arrays trimmed to the sizes used."""
+    si = _abi.StepIn()
+    si.n_max, si.n_a = int(n_max), len(a)
+    for i, v in enumerate(a):
+        si.a[i] = float(v)
+    si.m_W, si.t0, si.D, si.beta_D = float(m_W), float(t0), float(D), float(beta_D)
+    kv = kv if kv is not None else [0.0] * n_max
+    h = h if h is not None else [0.0] * n_max
+    phi = phi if phi is not None else [[0.0] * n_max, [0.0] * n_max]
+    for k in range(n_max):
+        si.kv[k], si.h[k] = float(kv[k]), float(h[k])
+        for p in range(2):
+            si.E[p][k], si.beta[p][k], si.phi[p][k] = float(E[p][k]), float(beta[p][k]), float(phi[p][k])
+    so = _abi.StepOut()
+    check("step_time_model", lib().step_time_model(ctypes.byref(si), ctypes.byref(so)))
+    na = len(a)
+    arr = lambda c, *shape: np.ctypeslib.as_array(c).reshape(*shape) if shape else np.ctypeslib.as_array(c)  # noqa
+    return {
+        "tau": np.array(so.tau)[:, :n_max].copy(),
+        "S": np.array(so.S)[:n_max].copy(),
+        "crossover": int(so.crossover),
+        "V": np.array(so.V)[:, :n_max].copy(),
+        "a0": np.array(so.a0).copy(),
+        "kstar": np.array(so.kstar)[:, :na].copy(),
+        "speedup": np.array(so.speedup)[:, :na].copy(),
+        "step_point": np.array(so.step_point)[:, :n_max].copy(),
+        "convex": np.array(so.convex).copy(),
+        "a1_convex": np.array(so.a1_convex).copy(),
+        "rho_star": np.array(so.rho_star)[:na, :n_max].copy(),
+        "rho_star_bytes": np.array(so.rho_star_bytes)[:na, :n_max].copy(),
+    }

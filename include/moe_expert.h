@@ -1,0 +1,232 @@
+/*
+ * moe_expert.h -- C ABI of the MoE expert operation of a speculative-decoding
+ * verification pass, for AMD Instinct MI355X (gfx950).
+ *
+ * Source of every definition below: Y. Lan, "Speculative Decoding for
+ * Mixture-of-Experts Models: Expert Bytes, Kernel Bandwidth and the Best Draft
+ * Length", arXiv:2610.34440 ("the paper").
+ *
+ * The expert operation (paper, Section 1): for a pass of n tokens, each routed to
+ * m of the layer's N experts, compute for every token t
+ *     y_t = sum_{j<m} w_tj * W_down[e_tj] ( silu(W_gate[e_tj] x_t) * (W_up[e_tj] x_t) )
+ * with silu(z) = z / (1 + exp(-z)).  A slot is one of a token's m selections, so a
+ * pass has n*m slots, numbered s = t*m + j.  Two kernels compute this same
+ * function:
+ *   - per-slot:       one read of the selected expert's weights per slot;
+ *   - deduplicating:  groups the pass's slots by expert and reads each distinct
+ *                     expert once, against all of that expert's tokens.
+ *
+ * Conventions shared by every device entry point:
+ *   - Pointers marked "device" are device memory owned by the caller; the
+ *     library keeps no pointer after the call returns and allocates nothing.
+ *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
+ *     the default stream).  A return value other than MOE_OK means nothing was
+ *     enqueued (except MOE_E_HIP, returned when a launch itself failed).
+ *   - Host-side validation happens before any launch.  No C++ exception crosses
+ *     this interface; no entry point aborts.
+ *   - Weights and x are bf16 (bit patterns, round-to-nearest-even) or fp32;
+ *     all accumulation is fp32; y is fp32.
+ *   - Weight layouts, row-major and contiguous:
+ *         W_gate, W_up : [N][d_ff][d_model]      W_down : [N][d_model][d_ff]
+ *     x : [n][d_model];  ids : [n][m] int32;  w : [n][m] fp32;  y : [n][d_model].
+ *   - Calls that share a workspace must not overlap in time.
+ */
+#ifndef MOE_EXPERT_H
+#define MOE_EXPERT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_E_INVAL = -1,     /* null pointer, size out of range, misaligned pointer */
+    MOE_E_DTYPE = -2,     /* unknown dtype, or d_model / d_ff not a multiple of 8 */
+    MOE_E_WORKSPACE = -3, /* workspace smaller than moe_workspace_bytes() */
+    MOE_E_HIP = -4,       /* a HIP launch failed */
+    MOE_E_IDS = -5        /* an expert id out of [0, N), or repeated within a token */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+enum { MOE_KIND_SLOT = 0, MOE_KIND_DEDUP = 1 };
+
+#define MOE_MAX_SLOTS 256     /* n * m */
+#define MOE_MAX_TOKENS 64     /* n */
+#define MOE_MAX_EXPERTS 1024  /* N */
+#define MOE_FLAG_ACCUMULATE 1u /* y += result (else y = result) */
+
+/* One MoE layer.  1 <= m <= N (m == N is allowed so that always-on shared
+ * experts can run as a layer whose every token selects all of them). */
+typedef struct {
+    int32_t N;       /* experts in the layer */
+    int32_t m;       /* experts selected per token */
+    int32_t d_model; /* d: token width; multiple of 8 */
+    int32_t d_ff;    /* expert hidden width; multiple of 8 */
+    int32_t dtype;   /* moe_dtype of the weights and of x */
+    uint32_t flags;  /* MOE_FLAG_* */
+} moe_layer_desc;
+
+/* Device pointers, caller-owned, 16-byte aligned, layouts as above. */
+typedef struct {
+    const void* w_gate;
+    const void* w_up;
+    const void* w_down;
+} moe_layer_weights;
+
+/*
+ * moe_route_group -- group the slots of a pass by expert (the deduplicating
+ * kernel "groups the pass's tokens by expert", paper Section 1; the union
+ * X(n) = |S_t u ... u S_{t+n-1}| is its number of groups, Section 1 "Routing,
+ * union and reuse").  One workgroup; bit-exact, deterministic.
+ *   ids            device [n*m]  expert id of slot s = t*m + j
+ *   count          device [N]    slots per expert (in-range slots only)
+ *   offset         device [N+1]  exclusive prefix sum of count; offset[N] = in-range slots
+ *   slot_by_expert device [n*m]  slots of expert e at [offset[e], offset[e+1]), in
+ *                                increasing s; entries from offset[N] on are -1
+ *   distinct       device [N]    experts with count > 0 in increasing id, then -1
+ *   u_and_err      device [2]    [0] = U (number of distinct experts),
+ *                                [1] = MOE_OK or MOE_E_IDS (an id outside [0, N), which
+ *                                      takes no part in the grouping, or an id repeated
+ *                                      within a token, which does)
+ * Limits: 1 <= n, 1 <= m <= N, n*m <= MOE_MAX_SLOTS, N <= MOE_MAX_EXPERTS.
+ */
+int moe_route_group(const int32_t* ids, int32_t n, int32_t m, int32_t N, int32_t* count,
+                    int32_t* offset, int32_t* slot_by_expert, int32_t* distinct,
+                    int32_t* u_and_err, void* hip_stream);
+
+/* Workspace bytes that moe_expert_perslot (kind MOE_KIND_SLOT) or
+ * moe_expert_dedup (MOE_KIND_DEDUP) needs for a pass of n tokens; 0 on invalid
+ * arguments.  The workspace holds the per-slot hidden activations and the
+ * per-slot expert outputs (fp32 or split bf16), n*m*(d_ff + d_model)*4 bytes
+ * plus alignment. */
+size_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t n, int32_t kind);
+
+/*
+ * moe_expert_perslot -- the expert operation by the per-slot kernel: every slot
+ * reads its expert's W_gate, W_up and W_down rows once (n*m expert reads per
+ * pass, paper Section 1 "Bytes": E_slot(n) = n m w).
+ *   x   device [n][d_model]  (dtype of desc)
+ *   ids device [n][m]        ids outside [0, N) are skipped (their slot adds 0)
+ *   w   device [n][m] fp32   routing weights
+ *   y   device [n][d_model] fp32, overwritten (or accumulated with MOE_FLAG_ACCUMULATE)
+ *   ws  device workspace of ws_bytes >= moe_workspace_bytes(desc, n, MOE_KIND_SLOT),
+ *       256-byte aligned; contents on entry are ignored.
+ * Per token, slot contributions are added in increasing j, so the result is
+ * deterministic and equal, bit for bit, to moe_expert_dedup's.
+ */
+int moe_expert_perslot(const moe_layer_desc* desc, const moe_layer_weights* weights,
+                       const void* x, const int32_t* ids, const float* w, int32_t n, float* y,
+                       void* ws, size_t ws_bytes, void* hip_stream);
+
+/*
+ * moe_expert_dedup -- the expert operation by the deduplicating kernel: each
+ * distinct expert of the pass is read once, against all of its tokens (paper
+ * Section 1; E_dedup = X(n) w).  offset, slot_by_expert, distinct and u_and_err
+ * are moe_route_group's outputs for the same ids (device).  Other arguments as
+ * for moe_expert_perslot.  When u_and_err[1] reports MOE_E_IDS the result for
+ * tokens with a repeated id includes the repeat; out-of-range slots add 0.
+ */
+int moe_expert_dedup(const moe_layer_desc* desc, const moe_layer_weights* weights, const void* x,
+                     const int32_t* ids, const float* w, int32_t n, const int32_t* offset,
+                     const int32_t* slot_by_expert, const int32_t* distinct,
+                     const int32_t* u_and_err, float* y, void* ws, size_t ws_bytes,
+                     void* hip_stream);
+
+/* Number of kernel launches moe_expert_perslot / moe_expert_dedup enqueue per
+ * call (moe_route_group is one more), or a negative status for a bad kind. */
+int moe_kernels_per_call(int32_t kind);
+
+/* As moe_expert_perslot / moe_expert_dedup, and also records hip events:
+ * events[0] before the first launch and events[i] after launch i, so
+ * n_events must be moe_kernels_per_call(kind) + 1.  `events` are hipEvent_t
+ * handles created by the caller.  For per-kernel timing. */
+int moe_expert_perslot_ev(const moe_layer_desc* desc, const moe_layer_weights* weights,
+                          const void* x, const int32_t* ids, const float* w, int32_t n, float* y,
+                          void* ws, size_t ws_bytes, void* hip_stream, void* const* events,
+                          int32_t n_events);
+int moe_expert_dedup_ev(const moe_layer_desc* desc, const moe_layer_weights* weights,
+                        const void* x, const int32_t* ids, const float* w, int32_t n,
+                        const int32_t* offset, const int32_t* slot_by_expert,
+                        const int32_t* distinct, const int32_t* u_and_err, float* y, void* ws,
+                        size_t ws_bytes, void* hip_stream, void* const* events,
+                        int32_t n_events);
+
+/*
+ * bytes_requested -- expert bytes the kernel `kind` requests for the pass whose
+ * ids (host [n][m]) are given (paper Section 1 "Bytes" and Section 3.1): with
+ * w = 3 d_model d_ff sizeof(W),
+ *     MOE_KIND_SLOT:  n m w           MOE_KIND_DEDUP:  X(n) w   (byte factor f = 1)
+ * x, y, ids and routing-weight bytes are not counted.  Host only, synchronous.
+ * Returns the byte count, or -MOE_E_* (negative) for invalid arguments or ids.
+ */
+int64_t bytes_requested(int32_t kind, const moe_layer_desc* desc, const int32_t* ids_host,
+                        int32_t n);
+
+/* ---------------------------------------------------------------------------
+ * step_time_model -- host-only evaluation of the paper's step-time model and
+ * best draft length (Sections 1, 3.1-3.4; Appendix B), in double.
+ *
+ *   tau_p(n) = t0 + D(n)/beta_D + E_p(n)/beta_p(n) + phi_p(n),  D(n) = D + kv(n-1)   (Eq. 5)
+ *   S(n)     = tau_slot(n) - tau_dedup(n)                                            (Eq. 6)
+ *   crossover = smallest n in [2, n_max] with S(n') > 0 for all n' in [n, n_max]; 0 = none
+ *   V_p(k)   = tau_p(k+1) + h(k);  V_p(0) = tau_slot(1) + h(0) for both kernels
+ *              (a one-token pass runs the same kernel either way, Section 3.1)
+ *   G_a(k)   = 1 + a + ... + a^k;  T_a(k) = G_a(k)/V(k);  k*(a) = smallest maximizer
+ *   a0_p     = V_p(1)/V_p(0) - 1                                                     (B.4)
+ *   speedup  = T_a(k*)/T_a(0)                                                        (Eq. 9)
+ *   step point a_j = max_{i<j} min_{k>=j} alpha_{k,i},
+ *              alpha_{k,i} = inf{a in [0,1) : T_a(k) > T_a(i)} (1 if empty)          (B.31)
+ *   a1_convex = min(c_1/V(0), 1), valid when 0 <= c_1 <= ... (convex = 1)            (B.36)
+ *   rho*_k(a) (Eq. 14, deduplicating engine):
+ *       1 - (B_k/(m W k)) [(G_a(k)-1) tau(1) - (kv(k)-kv(0))/beta_D - dphi_k] - (B_k/beta(1) - 1)/k
+ *       B_k = beta_dedup(k+1), beta(1) = beta_slot(1), tau(1) = tau_slot(1),
+ *       dphi_k = phi_dedup(k+1) - phi_slot(1)
+ *   rho*_k bytes (Eq. 16): 1 - [(G_a(k)-1)(D + m W + kv(0)) - (kv(k)-kv(0))]/(m W k)
+ * Indexing: arrays over n use index n-1; arrays over k use index k.
+ * Returns MOE_OK, or MOE_E_INVAL for sizes out of range or non-positive
+ * bandwidths / m W.  Pure function, thread-safe.
+ * ------------------------------------------------------------------------- */
+#define MOE_STEP_NMAX 16
+#define MOE_STEP_AMAX 64
+
+typedef struct {
+    int32_t n_max;                  /* pass sizes 1..n_max, 2 <= n_max <= MOE_STEP_NMAX */
+    int32_t n_a;                    /* acceptance grid points, 1..MOE_STEP_AMAX */
+    double a[MOE_STEP_AMAX];        /* acceptance values in [0, 1] */
+    double m_W;                     /* m W: expert bytes of one token over the layers, > 0 */
+    double t0;                      /* time outside memory reads */
+    double D;                       /* bytes read once per pass */
+    double kv[MOE_STEP_NMAX];       /* kv(k), k = 0..n_max-1 */
+    double beta_D;                  /* bandwidth of the D(n) bytes, > 0 */
+    double E[2][MOE_STEP_NMAX];     /* E_p(n), p = MOE_KIND_SLOT / MOE_KIND_DEDUP */
+    double beta[2][MOE_STEP_NMAX];  /* beta_p(n), > 0 */
+    double phi[2][MOE_STEP_NMAX];   /* phi_p(n) */
+    double h[MOE_STEP_NMAX];        /* h(k), k = 0..n_max-1 */
+} moe_step_in;
+
+typedef struct {
+    double tau[2][MOE_STEP_NMAX];
+    double S[MOE_STEP_NMAX];
+    int32_t crossover;
+    double V[2][MOE_STEP_NMAX];
+    double a0[2];
+    int32_t kstar[2][MOE_STEP_AMAX];
+    double speedup[2][MOE_STEP_AMAX];
+    double step_point[2][MOE_STEP_NMAX]; /* a_j at index j, j = 1..n_max-1 */
+    int32_t convex[2];
+    double a1_convex[2];
+    double rho_star[MOE_STEP_AMAX][MOE_STEP_NMAX];       /* [a index][k], k = 1..n_max-1 */
+    double rho_star_bytes[MOE_STEP_AMAX][MOE_STEP_NMAX]; /* [a index][k] */
+} moe_step_out;
+
+int step_time_model(const moe_step_in* in, moe_step_out* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EXPERT_H */

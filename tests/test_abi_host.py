@@ -1,0 +1,193 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every symbol
+the header declares, rejects bad arguments before any launch, and its host-only
+functions (bytes_requested, step_time_model) agree with the oracle."""
+import ctypes
+import os
+import random
+import re
+from fractions import Fraction as F
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import step_exact as se
+import expert_ffn_amd as efa
+from expert_ffn_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_expert.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|int64_t|size_t)\s+(\w+)\(", txt, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = _abi.lib()
+    names = _declared()
+    assert set(names) == set(_abi.EXPORTS)
+    for nm in names:
+        assert hasattr(L, nm), nm
+    out = os.popen("nm -D --defined-only %s" % _abi.SO_PATH).read()
+    for nm in names:
+        assert re.search(r"\bT %s\b" % nm, out), nm
+
+
+def _desc(**kw):
+    d = dict(N=8, m=2, d_model=64, d_ff=128, dtype=_abi.MOE_F32, flags=0)
+    d.update(kw)
+    return _abi.LayerDesc(d["N"], d["m"], d["d_model"], d["d_ff"], d["dtype"], d["flags"])
+
+
+def test_host_validation_rejects_before_launch():
+    L = _abi.lib()
+    vp = ctypes.c_void_p
+    fake = vp(0x1000)  # never dereferenced: validation fails first
+    W = _abi.LayerWeights(0x1000, 0x1000, 0x1000)
+    cases = [
+        (_desc(m=0), _abi.MOE_E_INVAL),
+        (_desc(m=9), _abi.MOE_E_INVAL),
+        (_desc(d_model=60), _abi.MOE_E_DTYPE),
+        (_desc(d_ff=100), _abi.MOE_E_DTYPE),
+        (_desc(dtype=7), _abi.MOE_E_DTYPE),
+        (_desc(flags=4), _abi.MOE_E_INVAL),
+        (_desc(N=2000, m=2), _abi.MOE_E_INVAL),
+    ]
+    for desc, want in cases:
+        st = L.moe_expert_perslot(ctypes.byref(desc), ctypes.byref(W), fake, fake, fake, 4, fake, fake, 1 << 30, None)
+        assert st == want
+    d = _desc()
+    # n out of range, n*m above the slot limit
+    assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 0, fake, fake, 1 << 30,
+                                None) == _abi.MOE_E_INVAL
+    assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 65, fake, fake, 1 << 30,
+                                None) == _abi.MOE_E_INVAL
+    # null pointer, misaligned pointer, small workspace
+    assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(W), None, fake, fake, 4, fake, fake, 1 << 30,
+                                None) == _abi.MOE_E_INVAL
+    Wm = _abi.LayerWeights(0x1004, 0x1000, 0x1000)
+    assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(Wm), fake, fake, fake, 4, fake, fake, 1 << 30,
+                                None) == _abi.MOE_E_INVAL
+    need = L.moe_workspace_bytes(ctypes.byref(d), 4, 0)
+    assert need == 4 * 2 * (64 + 128) * 4  # n m (d_ff + d) 4 bytes, 256-aligned pieces
+    assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 4, fake, fake, need - 1,
+                                None) == _abi.MOE_E_WORKSPACE
+    assert L.moe_expert_dedup(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 4, None, fake, fake, fake, fake,
+                              fake, need, None) == _abi.MOE_E_INVAL
+    # events: wrong count
+    ev = (vp * 2)(0x1, 0x2)
+    assert L.moe_expert_perslot_ev(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 4, fake, fake, need, None, ev,
+                                   2) == _abi.MOE_E_INVAL
+    assert L.moe_kernels_per_call(0) == 3 and L.moe_kernels_per_call(5) == _abi.MOE_E_INVAL
+    # grouping limits
+    assert L.moe_route_group(fake, 129, 2, 8, fake, fake, fake, fake, fake, None) == _abi.MOE_E_INVAL
+    assert L.moe_route_group(fake, 4, 9, 8, fake, fake, fake, fake, fake, None) == _abi.MOE_E_INVAL
+    assert L.moe_route_group(None, 4, 2, 8, fake, fake, fake, fake, fake, None) == _abi.MOE_E_INVAL
+
+
+@pytest.mark.parametrize("cfg", ["tiny", "dsv2lite", "qwen3", "mixtral"])
+def test_bytes_requested_matches_oracle(cfg):
+    import synth
+    from synth import routing
+    spec = synth.CONFIGS[cfg]
+    tr = routing.make_trace(spec, "correlated", 64, seed=4, p=0.5)
+    for n in range(1, 9):
+        for start in (0, 17, 40):
+            ids = tr.ids[start:start + n]
+            for kind in (0, 1):
+                got = efa.bytes_requested(kind, spec.N, spec.m, spec.d, spec.d_ff, spec.dtype, ids)
+                want = oracle.bytes_requested(kind, spec.N, spec.m, spec.d, spec.d_ff, spec.elem_bytes, ids)
+                assert got == want
+    bad = tr.ids[:2].copy()
+    bad[0, 0] = spec.N
+    with pytest.raises(efa.MoeError):
+        efa.bytes_requested(0, spec.N, spec.m, spec.d, spec.d_ff, spec.dtype, bad)
+    if spec.m > 1:
+        dup = tr.ids[:2].copy()
+        dup[1, 1] = dup[1, 0]
+        with pytest.raises(efa.MoeError):
+            efa.bytes_requested(1, spec.N, spec.m, spec.d, spec.d_ff, spec.dtype, dup)
+
+
+def _rand_model(rng, n_max):
+    E_slot = [rng.uniform(1, 2) * n for n in range(1, n_max + 1)]
+    U = [1.0]
+    for n in range(2, n_max + 1):
+        U.append(U[-1] + rng.uniform(0.3, 1.0))
+    E_dedup = [u for u in U]
+    b_slot = [rng.uniform(0.8, 1.2) for _ in range(n_max)]
+    b_dedup = [b_slot[0]] + [rng.uniform(0.4, 1.1) for _ in range(n_max - 1)]
+    kv = [rng.uniform(0, 0.05) * k for k in range(n_max)]
+    h = [rng.uniform(0, 0.1) for _ in range(n_max)]
+    phi = [[rng.uniform(0, 0.05) for _ in range(n_max)] for _ in range(2)]
+    return dict(E=[E_slot, E_dedup], beta=[b_slot, b_dedup], kv=kv, h=h, phi=phi,
+                t0=rng.uniform(0, 0.2), D=rng.uniform(0, 1), beta_D=rng.uniform(0.5, 2), m_W=E_slot[0])
+
+
+def test_step_time_model_matches_exact_oracle():
+    rng = random.Random(11)
+    a = [i / 21 for i in range(22)]
+    for trial in range(25):
+        n_max = rng.choice([3, 5, 8, 9])
+        M = _rand_model(rng, n_max)
+        out = efa.step_time_model(n_max, a, **M)
+        Fx = lambda v: F(v)  # noqa: E731  exact value of each double input
+        tau = [[se.tau(n, Fx(M["t0"]), Fx(M["D"]), [Fx(v) for v in M["kv"]], Fx(M["beta_D"]), Fx(M["E"][p][n - 1]),
+                       Fx(M["beta"][p][n - 1]), Fx(M["phi"][p][n - 1])) for n in range(1, n_max + 1)] for p in (0, 1)]
+        for p in (0, 1):
+            for n in range(n_max):
+                assert abs(out["tau"][p][n] - float(tau[p][n])) <= 1e-12 * float(tau[p][n])
+        S = {n: tau[0][n - 1] - tau[1][n - 1] for n in range(1, n_max + 1)}
+        assert out["crossover"] == se.crossover(S, n_max)
+        for p in (0, 1):
+            V = [tau[0][0] + Fx(M["h"][0])] + [tau[p][k] + Fx(M["h"][k]) for k in range(1, n_max)]
+            for k in range(n_max):
+                assert abs(out["V"][p][k] - float(V[k])) <= 1e-12 * float(V[k])
+            assert abs(out["a0"][p] - float(se.a0(V))) <= 1e-12
+            for ia, av in enumerate(a):
+                af = F(av)
+                ks = se.kstar(af, V)
+                # skip exact near-ties, where double rounding may pick the other maximizer
+                Ts = sorted((se.T(af, k, V) for k in range(n_max)), reverse=True)
+                if n_max > 1 and (Ts[0] - Ts[1]) <= F(1, 10 ** 9) * Ts[0]:
+                    continue
+                assert out["kstar"][p][ia] == ks
+                assert abs(out["speedup"][p][ia] - float(se.speedup(af, ks, V))) <= 1e-12
+            for j in range(1, n_max):
+                lo, hi = se.step_point_bracket(j, V)
+                assert float(lo) - 1e-12 <= out["step_point"][p][j] <= float(hi) + 1e-12
+            assert out["convex"][p] == int(se.is_convex_nondecreasing(V))
+            assert abs(out["a1_convex"][p] - float(se.a1_convex(V))) <= 1e-12
+        for ia, av in enumerate(a):
+            af = F(av)
+            for k in range(1, n_max):
+                want = se.rho_star_time(k, af, 1, Fx(M["m_W"]), tau[0][0], Fx(M["beta"][0][0]),
+                                        Fx(M["beta"][1][k]), Fx(M["kv"][k]) - Fx(M["kv"][0]), Fx(M["beta_D"]),
+                                        Fx(M["phi"][1][k]) - Fx(M["phi"][0][0]))
+                assert abs(out["rho_star"][ia][k] - float(want)) <= 1e-9 * max(1.0, abs(float(want)))
+                wb = se.rho_star_bytes(k, af, 1, Fx(M["m_W"]), Fx(M["D"]), [Fx(v) for v in M["kv"]])
+                assert abs(out["rho_star_bytes"][ia][k] - float(wb)) <= 1e-9 * max(1.0, abs(float(wb)))
+
+
+def test_step_time_model_printed_examples():
+    # Appendix B.3 'Jumps': V = (1, 2, 2) with one bandwidth: E_dedup = (1, 2, 2), beta = 1
+    out = efa.step_time_model(3, [0.5, 0.9], 1.0, E=[[1, 2, 3], [1, 2, 2]], beta=[[1, 1, 1], [1, 1, 1]])
+    assert list(out["V"][1]) == [1, 2, 2]
+    assert out["kstar"][1][0] == 0 and out["kstar"][1][1] == 2
+    # Appendix B.2: rho*_1 = 7/20, rho*_2 = 371/800 at a = 13/20 (byte form, m W = 1, D = kv = 0)
+    out = efa.step_time_model(3, [13 / 20], 1.0, E=[[1, 2, 3], [1, 2, 2]], beta=[[1, 1, 1], [1, 1, 1]])
+    assert abs(out["rho_star_bytes"][0][1] - 7 / 20) < 1e-15
+    assert abs(out["rho_star_bytes"][0][2] - 371 / 800) < 1e-15
+    # and the time form equals the byte form for one bandwidth and t0 = phi = 0
+    assert abs(out["rho_star"][0][1] - 7 / 20) < 1e-15 and abs(out["rho_star"][0][2] - 371 / 800) < 1e-15
+
+
+def test_step_time_model_rejects_bad_input():
+    with pytest.raises(efa.MoeError):
+        efa.step_time_model(1, [0.5], 1.0, E=[[1], [1]], beta=[[1], [1]])
+    with pytest.raises(efa.MoeError):
+        efa.step_time_model(2, [0.5], 1.0, E=[[1, 2], [1, 2]], beta=[[1, 0], [1, 1]])
+    with pytest.raises(efa.MoeError):
+        efa.step_time_model(2, [1.5], 1.0, E=[[1, 2], [1, 2]], beta=[[1, 1], [1, 1]])

@@ -1,0 +1,198 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: grouping bit-exact; y within rel-L2 5e-3 and max-abs 3e-2 of the fp32
+oracle on the same bf16-rounded inputs (fp32 layers: same bar); per-slot and
+deduplicating results bitwise equal (they add each token's slot outputs in the
+same order from identical per-slot products).
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import expert_ffn_amd as efa
+import oracle
+import synth
+from synth import routing
+from synth.device import to_torch
+
+from .gpu_cases import DeviceLayer, assert_close, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _ids_dev(ids):
+    return torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
+
+
+def _check_group(ids, N):
+    st, count, offset, sbe, distinct, U = oracle.route_group(ids, N)
+    g = efa.route_group(_ids_dev(ids), N)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.count.cpu().numpy(), count)
+    assert np.array_equal(g.offset.cpu().numpy(), offset)
+    assert np.array_equal(g.slot_by_expert.cpu().numpy(), sbe)
+    assert np.array_equal(g.distinct.cpu().numpy(), distinct)
+    ue = g.u_and_err.cpu().numpy()
+    assert ue[0] == U and ue[1] == (0 if st == oracle.OR_OK else efa._abi.MOE_E_IDS)
+
+
+def test_route_group_brute_force_small():
+    say("route_group brute force N=4 m=2 n=3")
+    pairs = list(itertools.permutations(range(4), 2))
+    for rows in itertools.product(pairs, repeat=3):
+        _check_group(np.array(rows, np.int32), 4)
+
+
+def test_route_group_configs_and_invalid():
+    rng = np.random.default_rng(0)
+    for N, m, n in [(8, 2, 1), (64, 6, 8), (128, 8, 8), (128, 8, 32), (1024, 4, 64), (16, 16, 16), (8, 2, 64)]:
+        say("route_group N=%d m=%d n=%d" % (N, m, n))
+        for _ in range(10):
+            ids = np.stack([rng.choice(N, m, replace=False) for _ in range(n)]).astype(np.int32)
+            _check_group(ids, N)
+    say("route_group invalid ids")
+    _check_group(np.array([[0, 7], [3, -1], [2, 2], [9, 1]], np.int32), 5)
+    _check_group(np.full((4, 2), 3, np.int32), 5)
+
+
+def _compare(dl, x, ids, w, what, shared=False, tokens=None, bitwise=True):
+    ys, yd, ue = dl.run(x, ids, w, shared=shared)
+    ref = dl.oracle_y(x, ids, w, shared=shared, tokens=tokens)
+    sel = slice(None) if tokens is None else tokens
+    r1 = assert_close(ys[sel], ref, what + " perslot")
+    r2 = assert_close(yd[sel], ref, what + " dedup")
+    if bitwise:
+        assert np.array_equal(ys, yd), what + ": per-slot and dedup differ bitwise"
+    return r1, r2
+
+
+def test_tiny_fp32_many_seeds():
+    spec = synth.CONFIGS["tiny"]
+    for seed in range(30):
+        say("tiny seed", seed)
+        dl = DeviceLayer(spec, seed)
+        tr = routing.uniform_trace(spec.N, spec.m, 4, routing.rng_for(seed, 0, "uniform"))
+        x = synth.pass_x(spec, seed, 0, 0, 4)
+        (rel, mx), _ = _compare(dl, x, tr.ids, tr.w, "tiny seed %d" % seed)
+        assert rel < 1e-5  # fp32 weights, fp32 MFMA: far inside the bar
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N,m,d,d_ff,n", [
+    (5, 3, 72, 136, 1), (5, 3, 72, 136, 3), (5, 3, 72, 136, 17), (6, 2, 40, 24, 33),
+    (4, 4, 8, 8, 64), (12, 4, 264, 200, 64), (9, 1, 1032, 40, 20)])
+def test_ragged_shapes(dtype, N, m, d, d_ff, n):
+    say("ragged", dtype, N, m, d, d_ff, n)
+    spec = synth.layer_spec("tiny", N=N, m=m, d=d, d_ff=d_ff, dtype=dtype, sigma=0.05)
+    dl = DeviceLayer(spec, 17)
+    tr = routing.correlated_trace(N, m, n, 0.7, routing.rng_for(17, 0, "correlated"))
+    x = synth.pass_x(spec, 17, 0, 1, n)
+    _compare(dl, x, tr.ids, tr.w, "ragged")
+
+
+def test_max_reuse_and_no_reuse():
+    spec = synth.layer_spec("tiny", N=70, m=4, d=128, d_ff=96, dtype="bf16")
+    dl = DeviceLayer(spec, 3)
+    rng = np.random.default_rng(3)
+    for n in (1, 8, 16, 17, 32, 33, 64):
+        say("max reuse n", n)
+        row = rng.choice(spec.N, spec.m, replace=False)
+        ids = np.tile(row, (n, 1)).astype(np.int32)  # every token the same experts: groups of n
+        w = rng.random((n, spec.m)).astype(np.float32)
+        x = synth.pass_x(spec, 3, 0, n, n)
+        _compare(dl, x, ids, w, "max reuse n=%d" % n)
+    say("no reuse n=17")
+    ids = np.arange(68, dtype=np.int32).reshape(17, 4)
+    w = rng.random((17, 4)).astype(np.float32)
+    _compare(dl, synth.pass_x(spec, 3, 0, 99, 17), ids, w, "no reuse")
+
+
+def test_invalid_ids_skip_slot_and_flag():
+    spec = synth.layer_spec("tiny", N=8, m=2, d=64, d_ff=64, dtype="bf16")
+    dl = DeviceLayer(spec, 5)
+    ids = np.array([[0, 3], [5, 9], [2, 1]], np.int32)   # slot (1,1) out of range
+    w = np.array([[0.5, 0.5], [0.7, 0.3], [0.6, 0.4]], np.float32)
+    x = synth.pass_x(spec, 5, 0, 0, 3)
+    say("invalid ids")
+    ys, yd, ue = dl.run(x, ids, w)
+    assert ue[1] == efa._abi.MOE_E_IDS and ue[0] == 5
+    ids_ok = ids.copy()
+    ids_ok[1, 1] = 7
+    w_ok = w.copy()
+    w_ok[1, 1] = 0.0  # the skipped slot adds nothing
+    ref = dl.oracle_y(x, ids_ok, w_ok)
+    assert_close(ys, ref, "invalid perslot")
+    assert_close(yd, ref, "invalid dedup")
+    assert np.array_equal(ys, yd)
+
+
+def test_accumulate_and_determinism():
+    spec = synth.layer_spec("tiny", N=16, m=4, d=256, d_ff=128, dtype="bf16")
+    dl = DeviceLayer(spec, 8)
+    tr = routing.uniform_trace(16, 4, 6, routing.rng_for(8, 0, "uniform"))
+    x = synth.pass_x(spec, 8, 0, 0, 6)
+    say("determinism")
+    a = dl.run(x, tr.ids, tr.w)
+    for _ in range(3):
+        b = dl.run(x, tr.ids, tr.w)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    say("accumulate")
+    xd = to_torch(x)
+    ids = _ids_dev(tr.ids)
+    w = torch.from_numpy(tr.w).cuda()
+    y0 = torch.randn(6, 256, device="cuda")
+    y = y0.clone()
+    efa.expert_perslot(dl.dev, xd, ids, w, y=y, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y.cpu(), (y0 + torch.from_numpy(a[0]).cuda()).cpu())
+
+
+# ------------------------------ full-size layers ------------------------------
+
+@pytest.fixture(scope="module")
+def dsv2():
+    say("upload dsv2lite layer")
+    return DeviceLayer(synth.CONFIGS["dsv2lite"], 2026, with_shared=True)
+
+
+@pytest.mark.parametrize("kind", ["uniform", "correlated"])
+def test_dsv2lite_windows(dsv2, kind):
+    spec = dsv2.spec
+    tr = routing.make_trace(spec, kind, 512, seed=2026, p=0.5)
+    starts = routing.window_starts(512, 8, 8, seed=2026)
+    for n in range(1, 9):
+        st = int(starts[n - 1])
+        ids, w = routing.window(tr, st, n)
+        x = synth.pass_x(spec, 2026, 0, 1000 + n, n)
+        say("dsv2lite", kind, "n", n, "start", st)
+        _compare(dsv2, x, ids, w, "dsv2lite %s n=%d" % (kind, n), shared=(n in (1, 5)))
+
+
+def test_qwen3_layer_zipf_and_tree():
+    spec = synth.CONFIGS["qwen3"]
+    say("upload qwen3 layer")
+    dl = DeviceLayer(spec, 77, layer=3)
+    tr = routing.make_trace(spec, "zipf", 256, seed=77, layer=3, s=1.1)
+    for n in (1, 2, 4, 8):
+        ids, w = routing.window(tr, 5 * n, n)
+        x = synth.pass_x(spec, 77, 3, n, n)
+        say("qwen3 zipf n", n)
+        _compare(dl, x, ids, w, "qwen3 n=%d" % n)
+    parents, ttr = routing.tree_routing(spec.N, spec.m, 0.5, routing.rng_for(77, 3, "tree"))
+    x = synth.pass_x(spec, 77, 3, 500, 32)
+    say("tree pass n=32")
+    _compare(dl, x, ttr.ids, ttr.w, "tree", tokens=[0, 1, 7, 19, 31])
+
+
+def test_mixtral_sampled_tokens():
+    spec = synth.CONFIGS["mixtral"]
+    say("upload mixtral layer")
+    dl = DeviceLayer(spec, 9)
+    tr = routing.make_trace(spec, "correlated", 64, seed=9, p=0.6)
+    for n, toks in ((1, [0]), (3, [0, 2]), (8, [1, 6])):
+        ids, w = routing.window(tr, 10, n)
+        x = synth.pass_x(spec, 9, 0, n, n)
+        say("mixtral n", n, "tokens", toks)
+        _compare(dl, x, ids, w, "mixtral n=%d" % n, tokens=toks)
