@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE expert operation of a verification pass on one MI355X.
+
+Metric: achieved HBM GB/s of the expert operation and its fraction of the
+8 TB/s peak, against pass size n = 1..8, for the per-slot and the deduplicating
+kernel; the bandwidth ratio r(n) = beta_dedup / beta_slot, the byte share
+u(n) = E_dedup / E_slot, the saving S(n) = t_slot - t_dedup and the crossover n
+(Lan, arXiv:2610.34440, Sections 1-3).
+
+One step = for each routing kind of the layer and each n = 1..8, one pass copied
+from a window of the routing trace, run once by each kernel.  Every pass is timed
+alone with HIP events on the launch stream, after a read-only 1 GiB cache flush
+(the 256 MB Infinity Cache would otherwise hold a whole pass; a flush that also
+writes would leave dirty lines whose write-back competes with the timed reads).  Bytes are requested
+expert bytes: n m w per-slot, X(n) w deduplicating (w = 3 d d_ff 2 B).
+beta, r and u are from bytes and times summed over the timed passes.
+
+Prints one JSON line.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "expert-op achieved HBM GB/s & % peak vs pass size n=1..8; dedup r(n), crossover n"
+SCRUB_BYTES = 1 << 30
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (torch's Event only sees torch's own streams)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pool = []
+
+    def make(self, k):
+        out = []
+        for _ in range(k):
+            e = ctypes.c_void_p()
+            assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+            self.pool.append(e)
+            out.append(e.value)
+        return out
+
+    def record(self, ev, stream):
+        assert self.h.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) == 0
+
+    def ms(self, a, b):
+        self.h.hipEventSynchronize(ctypes.c_void_p(b))
+        f = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return float(f.value)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in ("expert_ffn_amd/csrc/moe_expert.hip",):
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(spec, host_w, passes, budget_s):
+    """The oracle, as it stands, on host cores over a bounded sample of passes."""
+    import oracle
+    t0 = time.perf_counter()
+    nbytes = 0
+    done = 0
+    for (x_h, ids, w) in passes:
+        oracle.moe_ffn(*host_w, x_h, ids, w, spec.dtype)
+        nbytes += ids.size * spec.expert_bytes
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d passes (n=1..8 windows of the same traces), %.1f s, requested per-slot weight bytes / "
+                      "wall time, single-threaded C oracle (double accumulate)" % (done, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=8)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="dsv2lite", choices=["dsv2lite", "qwen3", "mixtral"])
+    ap.add_argument("--nmax", type=int, default=8)
+    ap.add_argument("--seed", type=int, default=2026)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-scrub", action="store_true")
+    ap.add_argument("--details", default="", help="write per-pass records (JSONL) here")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the expert operation here runs on a single MI355X and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import expert_ffn_amd as efa
+    import synth
+    from synth import routing
+    from synth.device import to_torch
+
+    torch.cuda.set_device(0)
+    spec = synth.CONFIGS[args.config]
+    kinds = {"dsv2lite": [("uniform", {}), ("correlated", {"p": 0.5})],
+             "qwen3": [("zipf", {"s": 1.1})],
+             "mixtral": [("uniform", {}), ("correlated", {"p": 0.6})]}[args.config]
+    T = 4096
+    t_setup = time.perf_counter()
+    host_w = synth.layer_weights(spec, args.seed)
+    layer = efa.Layer(*(to_torch(a) for a in host_w), m=spec.m)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    nsteps_total = args.warmup + args.steps
+    nvals = list(range(1, args.nmax + 1))
+
+    # inputs resident in HBM before timing: one window per (kind, n, step)
+    passes = {}
+    host_passes = []
+    for ki, (kind, kw) in enumerate(kinds):
+        tr = routing.make_trace(spec, kind, T, seed=args.seed, **kw)
+        for n in nvals:
+            starts = routing.window_starts(T, n, nsteps_total, seed=args.seed + 17 * ki)
+            for s in range(nsteps_total):
+                ids, w = routing.window(tr, int(starts[s]), n)
+                x_h = synth.pass_x(spec, args.seed, 0, 10000 * ki + 100 * n + s, n)
+                dev = (to_torch(x_h), torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda())
+                passes[(kind, n, s)] = dict(x=dev[0], ids=dev[1], w=dev[2], ids_h=ids,
+                                            U=len(set(ids.reshape(-1).tolist())))
+                if s == 0:
+                    host_passes.append((x_h, ids, w))
+    ws = layer.workspace(nvals[-1])  # zero-filled once; serves every n
+    ys = {n: torch.empty(n, spec.d, dtype=torch.float32, device="cuda") for n in nvals}
+    scrub = torch.ones(SCRUB_BYTES // 4, dtype=torch.float32, device="cuda")
+    scrub_out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def flush():
+        torch.sum(scrub, dim=0, out=scrub_out)  # reads 1 GiB, writes 4 bytes
+    info = torch.zeros(3, dtype=torch.int32, device="cuda")
+    ev = HipEvents()
+    nk = efa.kernels_per_call(efa.MOE_KIND_SLOT)
+    assert nk == 1 and efa.kernels_per_call(efa.MOE_KIND_DEDUP) == 1
+    ev_slot = ev.make(2)
+    ev_dedup = ev.make(2)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    w_exp = spec.expert_bytes
+    recs = []
+
+    def run_step(s, record):
+        for kind, _ in kinds:
+            for n in nvals:
+                p = passes[(kind, n, s)]
+                if not args.no_scrub:
+                    flush()
+                efa.expert_perslot(layer, p["x"], p["ids"], p["w"], y=ys[n], ws=ws, stream=stream, events=ev_slot)
+                t_slot = ev.ms(ev_slot[0], ev_slot[1])
+                if not args.no_scrub:
+                    flush()
+                efa.expert_dedup(layer, p["x"], p["ids"], p["w"], y=ys[n], ws=ws, info=info, stream=stream,
+                                 events=ev_dedup)
+                t_dedup = ev.ms(ev_dedup[0], ev_dedup[1])
+                if record:
+                    recs.append(dict(kind=kind, n=n, step=s, U=p["U"], bytes_slot=n * spec.m * w_exp,
+                                     bytes_dedup=p["U"] * w_exp, t_slot_ms=t_slot, t_dedup_ms=t_dedup))
+
+    for s in range(args.warmup):
+        run_step(s, False)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for s in range(args.warmup, nsteps_total):
+        run_step(s, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+
+    # aggregate (bytes and times summed over the timed passes)
+    per_kind = {}
+    for kind, _ in kinds:
+        rows = []
+        S = {}
+        for n in nvals:
+            R = [r for r in recs if r["kind"] == kind and r["n"] == n]
+            bs, bd = sum(r["bytes_slot"] for r in R), sum(r["bytes_dedup"] for r in R)
+            ts, td = sum(r["t_slot_ms"] for r in R) / 1e3, sum(r["t_dedup_ms"] for r in R) / 1e3
+            gs, gd = bs / ts / 1e9, bd / td / 1e9
+            S[n] = (ts - td) / len(R)
+            rows.append(dict(n=n, gbps_slot=round(gs, 1), gbps_dedup=round(gd, 1),
+                             frac_slot=round(gs / PEAK_HBM_GBPS, 4), frac_dedup=round(gd / PEAK_HBM_GBPS, 4),
+                             r=round(gd / gs, 4), u=round(bd / bs, 4),
+                             us_slot=round(ts / len(R) * 1e6, 2), us_dedup=round(td / len(R) * 1e6, 2),
+                             mean_U=round(sum(r["U"] for r in R) / len(R), 2)))
+        cross = 0
+        for n in range(nvals[-1], 1, -1):
+            if S[n] > 0:
+                cross = n
+            else:
+                break
+        per_kind[kind] = dict(per_n=rows, crossover=cross)
+
+    tot_bytes = sum(r["bytes_slot"] + r["bytes_dedup"] for r in recs)
+    tot_s = sum(r["t_slot_ms"] + r["t_dedup_ms"] for r in recs) / 1e3
+    value = tot_bytes / tot_s / 1e9
+    ms_per_step = tot_s * 1e3 / args.steps
+
+    # dominant kernel: the per-slot launch (one fused kernel per pass)
+    n_launch = len(recs)
+    slot_bytes = sum(r["bytes_slot"] for r in recs)
+    slot_s = sum(r["t_slot_ms"] for r in recs) / 1e3
+    dd_bytes = sum(r["bytes_dedup"] for r in recs)
+    dd_s = sum(r["t_dedup_ms"] for r in recs) / 1e3
+    achieved = slot_bytes / slot_s / 1e9
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic_k_expert_perslot_%s.json" % args.config)
+    if os.path.exists(tpath):
+        tj = json.load(open(tpath))
+        if tj.get("source_hash") == source_hash():
+            traffic = tj.get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                "kernel": "k_expert<bf16, per-slot> (whole operation, one launch)", "launches": n_launch,
+                "avg_launch_us": round(slot_s / n_launch * 1e6, 3),
+                "algorithmic_bytes_per_launch": round(slot_bytes / n_launch, 1),
+                "dedup_kernel": {"achieved": round(dd_bytes / dd_s / 1e9, 1),
+                                 "avg_launch_us": round(dd_s / n_launch * 1e6, 3),
+                                 "algorithmic_bytes_per_launch": round(dd_bytes / n_launch, 1)}}
+
+    cpu = cpu_baseline(spec, host_w, host_passes, args.cpu_budget)
+
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "%s-shaped MoE layer expert op, n=1..%d, routing %s" % (
+               args.config, nvals[-1], "+".join(k for k, _ in kinds)),
+               "N": spec.N, "m": spec.m, "d_model": spec.d, "d_ff": spec.d_ff, "passes_per_step": len(kinds) * len(nvals) * 2,
+               "scrub_bytes": 0 if args.no_scrub else SCRUB_BYTES},
+           "roofline": roofline, "cpu_baseline": cpu, "results": per_kind,
+           "wall_s_timed": round(wall, 3), "setup_s": round(setup_s, 1), "source_hash": source_hash()}
+    if args.details:
+        with open(args.details, "w") as f:
+            for r in recs:
+                f.write(json.dumps(r) + "\n")
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -79,15 +79,15 @@ def lib():
             L.moe_route_group.restype = ctypes.c_int
             L.moe_workspace_bytes.argtypes = [pdesc, i32, i32]
             L.moe_workspace_bytes.restype = sz
-            L.moe_expert_perslot.argtypes = [pdesc, pw, vp, vp, vp, i32, vp, vp, sz, vp]
+            L.moe_expert_perslot.argtypes = [pdesc, pw, vp, vp, vp, i32, vp, vp, vp, sz, vp]
             L.moe_expert_perslot.restype = ctypes.c_int
-            L.moe_expert_dedup.argtypes = [pdesc, pw, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+            L.moe_expert_dedup.argtypes = [pdesc, pw, vp, vp, vp, i32, vp, vp, vp, sz, vp]
             L.moe_expert_dedup.restype = ctypes.c_int
             L.moe_kernels_per_call.argtypes = [i32]
             L.moe_kernels_per_call.restype = ctypes.c_int
-            L.moe_expert_perslot_ev.argtypes = [pdesc, pw, vp, vp, vp, i32, vp, vp, sz, vp, vp, i32]
+            L.moe_expert_perslot_ev.argtypes = [pdesc, pw, vp, vp, vp, i32, vp, vp, vp, sz, vp, vp, i32]
             L.moe_expert_perslot_ev.restype = ctypes.c_int
-            L.moe_expert_dedup_ev.argtypes = [pdesc, pw, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp, vp, i32]
+            L.moe_expert_dedup_ev.argtypes = [pdesc, pw, vp, vp, vp, i32, vp, vp, vp, sz, vp, vp, i32]
             L.moe_expert_dedup_ev.restype = ctypes.c_int
             L.bytes_requested.argtypes = [i32, pdesc, vp, i32]
             L.bytes_requested.restype = i64

@@ -65,10 +65,11 @@ class Layer:
         return 3 * self.d * self.d_ff * self.w_gate.element_size()
 
     def workspace(self, n, kind=MOE_KIND_SLOT):
-        nb = lib().moe_workspace_bytes(ctypes.byref(self.desc()), int(n), int(kind))
+        """Zero-filled workspace for passes of up to n tokens (either kind)."""
+        nb = max(lib().moe_workspace_bytes(ctypes.byref(self.desc()), int(n), int(k)) for k in (0, 1))
         if nb == 0:
             raise _abi.MoeError("moe_workspace_bytes", _abi.MOE_E_INVAL)
-        return torch.empty(nb, dtype=torch.uint8, device=self.w_gate.device)
+        return torch.zeros(nb, dtype=torch.uint8, device=self.w_gate.device)
 
 
 def route_group(ids, N, out=None, stream=None):
@@ -106,36 +107,37 @@ def _events(events):
     return arr, len(events)
 
 
-def expert_perslot(layer, x, ids, w, y=None, ws=None, accumulate=False, stream=None, events=None):
-    """The expert operation by the per-slot kernel; returns y [n][d] fp32."""
-    n, y, ws = _prep(layer, x, ids, w, y, ws, MOE_KIND_SLOT)
+def _run(fn, fn_ev, layer, x, ids, w, y, ws, info, accumulate, stream, events, kind, where):
+    n, y, ws = _prep(layer, x, ids, w, y, ws, kind)
+    if info is not None:
+        _check_dev("info", info, torch.int32, (3,))
     desc = layer.desc(accumulate)
+    args = [ctypes.byref(desc), ctypes.byref(layer._weights), _vp(x), _vp(ids), _vp(w), n, _vp(y), _vp(info),
+            _vp(ws), ws.numel(), _stream(stream)]
     if events is None:
-        st = lib().moe_expert_perslot(ctypes.byref(desc), ctypes.byref(layer._weights), _vp(x), _vp(ids), _vp(w), n,
-                                      _vp(y), _vp(ws), ws.numel(), _stream(stream))
+        st = fn(*args)
     else:
         ev, nev = _events(events)
-        st = lib().moe_expert_perslot_ev(ctypes.byref(desc), ctypes.byref(layer._weights), _vp(x), _vp(ids), _vp(w),
-                                         n, _vp(y), _vp(ws), ws.numel(), _stream(stream), ev, nev)
-    check("moe_expert_perslot", st)
+        st = fn_ev(*args, ev, nev)
+    check(where, st)
     return y
 
 
-def expert_dedup(layer, x, ids, w, grouping, y=None, ws=None, accumulate=False, stream=None, events=None):
-    """The expert operation by the deduplicating kernel, given route_group's
-    output for the same ids; returns y [n][d] fp32."""
-    n, y, ws = _prep(layer, x, ids, w, y, ws, MOE_KIND_DEDUP)
-    g = grouping
-    desc = layer.desc(accumulate)
-    args = [ctypes.byref(desc), ctypes.byref(layer._weights), _vp(x), _vp(ids), _vp(w), n, _vp(g.offset),
-            _vp(g.slot_by_expert), _vp(g.distinct), _vp(g.u_and_err), _vp(y), _vp(ws), ws.numel(), _stream(stream)]
-    if events is None:
-        st = lib().moe_expert_dedup(*args)
-    else:
-        ev, nev = _events(events)
-        st = lib().moe_expert_dedup_ev(*args, ev, nev)
-    check("moe_expert_dedup", st)
-    return y
+def expert_perslot(layer, x, ids, w, y=None, ws=None, info=None, accumulate=False, stream=None, events=None):
+    """The expert operation by the per-slot kernel (one launch); returns y [n][d] fp32.
+    ``ws`` must come from ``layer.workspace`` (zero-filled); ``info`` an int32 [3]
+    device tensor receiving (U, ids status, sync status)."""
+    L = lib()
+    return _run(L.moe_expert_perslot, L.moe_expert_perslot_ev, layer, x, ids, w, y, ws, info, accumulate, stream,
+                events, MOE_KIND_SLOT, "moe_expert_perslot")
+
+
+def expert_dedup(layer, x, ids, w, y=None, ws=None, info=None, accumulate=False, stream=None, events=None):
+    """The expert operation by the deduplicating kernel (one launch; the grouping
+    by expert runs inside it); returns y [n][d] fp32."""
+    L = lib()
+    return _run(L.moe_expert_dedup, L.moe_expert_dedup_ev, layer, x, ids, w, y, ws, info, accumulate, stream,
+                events, MOE_KIND_DEDUP, "moe_expert_dedup")
 
 
 def kernels_per_call(kind):

@@ -29,7 +29,10 @@
  *   - Weight layouts, row-major and contiguous:
  *         W_gate, W_up : [N][d_ff][d_model]      W_down : [N][d_model][d_ff]
  *     x : [n][d_model];  ids : [n][m] int32;  w : [n][m] fp32;  y : [n][d_model].
- *   - Calls that share a workspace must not overlap in time.
+ *   - Workspaces (`ws`) are caller-owned device memory that must be zero-filled
+ *     once before first use (e.g. hipMemset); every call that runs to completion
+ *     leaves the workspace's synchronisation words zero again.  Calls that share
+ *     a workspace must not overlap in time.
  */
 #ifndef MOE_EXPERT_H
 #define MOE_EXPERT_H
@@ -46,7 +49,7 @@ typedef enum {
     MOE_E_INVAL = -1,     /* null pointer, size out of range, misaligned pointer */
     MOE_E_DTYPE = -2,     /* unknown dtype, or d_model / d_ff not a multiple of 8 */
     MOE_E_WORKSPACE = -3, /* workspace smaller than moe_workspace_bytes() */
-    MOE_E_HIP = -4,       /* a HIP launch failed */
+    MOE_E_HIP = -4,       /* a HIP launch failed, or (in info) an internal wait expired */
     MOE_E_IDS = -5        /* an expert id out of [0, N), or repeated within a token */
 } moe_status;
 
@@ -100,44 +103,49 @@ int moe_route_group(const int32_t* ids, int32_t n, int32_t m, int32_t N, int32_t
 
 /* Workspace bytes that moe_expert_perslot (kind MOE_KIND_SLOT) or
  * moe_expert_dedup (MOE_KIND_DEDUP) needs for a pass of n tokens; 0 on invalid
- * arguments.  The workspace holds the per-slot hidden activations and the
- * per-slot expert outputs (fp32 or split bf16), n*m*(d_ff + d_model)*4 bytes
- * plus alignment. */
+ * arguments.  The workspace holds 160 KB of synchronisation counters (one per
+ * 128-byte line), the per-slot hidden activations and the per-slot expert outputs:
+ * 163840 + n*m*(d_ff + d_model)*4 bytes plus alignment.  A workspace sized for n
+ * serves every smaller n of the same layer.  d_model is limited to 16384. */
 size_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t n, int32_t kind);
 
 /*
  * moe_expert_perslot -- the expert operation by the per-slot kernel: every slot
  * reads its expert's W_gate, W_up and W_down rows once (n*m expert reads per
- * pass, paper Section 1 "Bytes": E_slot(n) = n m w).
- *   x   device [n][d_model]  (dtype of desc)
- *   ids device [n][m]        ids outside [0, N) are skipped (their slot adds 0)
- *   w   device [n][m] fp32   routing weights
- *   y   device [n][d_model] fp32, overwritten (or accumulated with MOE_FLAG_ACCUMULATE)
- *   ws  device workspace of ws_bytes >= moe_workspace_bytes(desc, n, MOE_KIND_SLOT),
- *       256-byte aligned; contents on entry are ignored.
+ * pass, paper Section 1 "Bytes": E_slot(n) = n m w).  One kernel launch.
+ *   x    device [n][d_model]  (dtype of desc)
+ *   ids  device [n][m]        ids outside [0, N) are skipped (their slot adds 0)
+ *   w    device [n][m] fp32   routing weights
+ *   y    device [n][d_model] fp32, overwritten (or accumulated with MOE_FLAG_ACCUMULATE)
+ *   info device [3] int32 or NULL: [0] = U, the number of distinct in-range experts
+ *        of the pass; [1] = MOE_OK or MOE_E_IDS (an id outside [0, N) or repeated
+ *        within a token); [2] = MOE_OK, or MOE_E_HIP when an internal bounded wait
+ *        expired (only with a workspace that was not zero-filled); y is then invalid
+ *        and the workspace must be zero-filled again
+ *   ws   device workspace, ws_bytes >= moe_workspace_bytes(desc, n, MOE_KIND_SLOT),
+ *        256-byte aligned, zero-filled before first use (see above).
  * Per token, slot contributions are added in increasing j, so the result is
  * deterministic and equal, bit for bit, to moe_expert_dedup's.
  */
 int moe_expert_perslot(const moe_layer_desc* desc, const moe_layer_weights* weights,
                        const void* x, const int32_t* ids, const float* w, int32_t n, float* y,
-                       void* ws, size_t ws_bytes, void* hip_stream);
+                       int32_t* info, void* ws, size_t ws_bytes, void* hip_stream);
 
 /*
- * moe_expert_dedup -- the expert operation by the deduplicating kernel: each
- * distinct expert of the pass is read once, against all of its tokens (paper
- * Section 1; E_dedup = X(n) w).  offset, slot_by_expert, distinct and u_and_err
- * are moe_route_group's outputs for the same ids (device).  Other arguments as
- * for moe_expert_perslot.  When u_and_err[1] reports MOE_E_IDS the result for
- * tokens with a repeated id includes the repeat; out-of-range slots add 0.
+ * moe_expert_dedup -- the expert operation by the deduplicating kernel: the
+ * pass's slots are grouped by expert (the grouping of moe_route_group, computed
+ * inside the same launch) and each distinct expert is read once, against all of
+ * its tokens (paper Section 1; E_dedup = X(n) w).  Arguments as for
+ * moe_expert_perslot, workspace kind MOE_KIND_DEDUP.  With MOE_E_IDS in info[1],
+ * a token's repeated id counts as often as it appears; out-of-range slots add 0.
  */
 int moe_expert_dedup(const moe_layer_desc* desc, const moe_layer_weights* weights, const void* x,
-                     const int32_t* ids, const float* w, int32_t n, const int32_t* offset,
-                     const int32_t* slot_by_expert, const int32_t* distinct,
-                     const int32_t* u_and_err, float* y, void* ws, size_t ws_bytes,
-                     void* hip_stream);
+                     const int32_t* ids, const float* w, int32_t n, float* y, int32_t* info,
+                     void* ws, size_t ws_bytes, void* hip_stream);
 
 /* Number of kernel launches moe_expert_perslot / moe_expert_dedup enqueue per
- * call (moe_route_group is one more), or a negative status for a bad kind. */
+ * call (moe_route_group is a separate, optional launch), or a negative status for
+ * a bad kind. */
 int moe_kernels_per_call(int32_t kind);
 
 /* As moe_expert_perslot / moe_expert_dedup, and also records hip events:
@@ -146,14 +154,12 @@ int moe_kernels_per_call(int32_t kind);
  * handles created by the caller.  For per-kernel timing. */
 int moe_expert_perslot_ev(const moe_layer_desc* desc, const moe_layer_weights* weights,
                           const void* x, const int32_t* ids, const float* w, int32_t n, float* y,
-                          void* ws, size_t ws_bytes, void* hip_stream, void* const* events,
-                          int32_t n_events);
+                          int32_t* info, void* ws, size_t ws_bytes, void* hip_stream,
+                          void* const* events, int32_t n_events);
 int moe_expert_dedup_ev(const moe_layer_desc* desc, const moe_layer_weights* weights,
-                        const void* x, const int32_t* ids, const float* w, int32_t n,
-                        const int32_t* offset, const int32_t* slot_by_expert,
-                        const int32_t* distinct, const int32_t* u_and_err, float* y, void* ws,
-                        size_t ws_bytes, void* hip_stream, void* const* events,
-                        int32_t n_events);
+                        const void* x, const int32_t* ids, const float* w, int32_t n, float* y,
+                        int32_t* info, void* ws, size_t ws_bytes, void* hip_stream,
+                        void* const* events, int32_t n_events);
 
 /*
  * bytes_requested -- expert bytes the kernel `kind` requests for the pass whose

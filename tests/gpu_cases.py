@@ -12,6 +12,7 @@ from synth.device import to_torch
 
 REL_L2_TOL = 5e-3   # relative L2 error bound on y (bf16 weights, fp32 accumulate)
 MAX_ABS_TOL = 3e-2  # max abs error bound on y
+SYNC_BYTES = 4 * 32 * (256 + 1024)  # counter area at the start of a workspace
 
 
 def say(*a):
@@ -33,23 +34,29 @@ class DeviceLayer:
             self.shared_dev = efa.Layer(*(to_torch(a) for a in self.shared_host), m=spec.n_shared)
 
     def run(self, x_host, ids_host, w_host, shared=False, stream=None):
-        """Returns (y_perslot, y_dedup, u_and_err) on the host."""
+        """Returns (y_perslot, y_dedup, info_dedup) on the host; info = (U, ids status, sync status)."""
         x = to_torch(x_host)
         ids = torch.from_numpy(np.ascontiguousarray(ids_host, np.int32)).cuda()
         w = torch.from_numpy(np.ascontiguousarray(w_host, np.float32)).cuda()
-        ys = efa.expert_perslot(self.dev, x, ids, w, stream=stream)
-        grp = efa.route_group(ids, self.spec.N, stream=stream)
-        yd = efa.expert_dedup(self.dev, x, ids, w, grp, stream=stream)
+        n = x.shape[0]
+        ws = self.dev.workspace(n)
+        info_s = torch.full((3,), 99, dtype=torch.int32, device="cuda")
+        info_d = torch.full((3,), 99, dtype=torch.int32, device="cuda")
+        ys = efa.expert_perslot(self.dev, x, ids, w, ws=ws, info=info_s, stream=stream)
+        yd = efa.expert_dedup(self.dev, x, ids, w, ws=ws, info=info_d, stream=stream)
         if shared:
-            n = x.shape[0]
             E = self.spec.n_shared
             sids = torch.arange(E, dtype=torch.int32, device="cuda").repeat(n, 1).contiguous()
             sw = torch.ones(n, E, dtype=torch.float32, device="cuda")
-            sg = efa.route_group(sids, E, stream=stream)
-            efa.expert_dedup(self.shared_dev, x, sids, sw, sg, y=ys, accumulate=True, stream=stream)
-            efa.expert_dedup(self.shared_dev, x, sids, sw, sg, y=yd, accumulate=True, stream=stream)
+            sws = self.shared_dev.workspace(n)
+            efa.expert_dedup(self.shared_dev, x, sids, sw, y=ys, ws=sws, accumulate=True, stream=stream)
+            efa.expert_dedup(self.shared_dev, x, sids, sw, y=yd, ws=sws, accumulate=True, stream=stream)
         torch.cuda.synchronize()
-        return ys.cpu().numpy(), yd.cpu().numpy(), grp.u_and_err.cpu().numpy()
+        info_s, info_d = info_s.cpu().numpy(), info_d.cpu().numpy()
+        assert np.array_equal(info_s, info_d), (info_s, info_d)
+        assert info_d[2] == 0, "internal wait expired"
+        assert np.all(ws[:SYNC_BYTES].cpu().numpy() == 0), "sync words not reset"
+        return ys.cpu().numpy(), yd.cpu().numpy(), info_d
 
     def oracle_y(self, x_host, ids_host, w_host, shared=False, tokens=None):
         """fp32 oracle output, for all tokens or the listed ones."""

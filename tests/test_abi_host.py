@@ -56,31 +56,38 @@ def test_host_validation_rejects_before_launch():
         (_desc(N=2000, m=2), _abi.MOE_E_INVAL),
     ]
     for desc, want in cases:
-        st = L.moe_expert_perslot(ctypes.byref(desc), ctypes.byref(W), fake, fake, fake, 4, fake, fake, 1 << 30, None)
+        st = L.moe_expert_perslot(ctypes.byref(desc), ctypes.byref(W), fake, fake, fake, 4, fake, None, fake, 1 << 30,
+                                  None)
         assert st == want
     d = _desc()
     # n out of range, n*m above the slot limit
-    assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 0, fake, fake, 1 << 30,
+    assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 0, fake, None, fake, 1 << 30,
                                 None) == _abi.MOE_E_INVAL
-    assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 65, fake, fake, 1 << 30,
+    assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 65, fake, None, fake, 1 << 30,
                                 None) == _abi.MOE_E_INVAL
-    # null pointer, misaligned pointer, small workspace
-    assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(W), None, fake, fake, 4, fake, fake, 1 << 30,
+    # null pointer, misaligned pointer, small workspace, misaligned workspace
+    assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(W), None, fake, fake, 4, fake, None, fake, 1 << 30,
                                 None) == _abi.MOE_E_INVAL
     Wm = _abi.LayerWeights(0x1004, 0x1000, 0x1000)
-    assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(Wm), fake, fake, fake, 4, fake, fake, 1 << 30,
+    assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(Wm), fake, fake, fake, 4, fake, None, fake, 1 << 30,
                                 None) == _abi.MOE_E_INVAL
     need = L.moe_workspace_bytes(ctypes.byref(d), 4, 0)
-    assert need == 4 * 2 * (64 + 128) * 4  # n m (d_ff + d) 4 bytes, 256-aligned pieces
-    assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 4, fake, fake, need - 1,
+    assert need == 163840 + 4 * 2 * 128 * 4 + 4 * 2 * 64 * 4  # sync area + h + O (256-aligned pieces)
+    assert L.moe_workspace_bytes(ctypes.byref(d), 4, 1) == need
+    assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 4, fake, None, fake, need - 1,
                                 None) == _abi.MOE_E_WORKSPACE
-    assert L.moe_expert_dedup(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 4, None, fake, fake, fake, fake,
-                              fake, need, None) == _abi.MOE_E_INVAL
-    # events: wrong count
-    ev = (vp * 2)(0x1, 0x2)
-    assert L.moe_expert_perslot_ev(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 4, fake, fake, need, None, ev,
-                                   2) == _abi.MOE_E_INVAL
-    assert L.moe_kernels_per_call(0) == 3 and L.moe_kernels_per_call(5) == _abi.MOE_E_INVAL
+    assert L.moe_expert_dedup(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 4, fake, None, vp(0x1010), need,
+                              None) == _abi.MOE_E_INVAL
+    assert L.moe_expert_dedup(ctypes.byref(d), ctypes.byref(W), fake, None, fake, 4, fake, None, fake, need,
+                              None) == _abi.MOE_E_INVAL
+    # events: wrong count, null events
+    ev = (vp * 3)(0x1, 0x2, 0x3)
+    assert L.moe_expert_perslot_ev(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 4, fake, None, fake, need,
+                                   None, ev, 3) == _abi.MOE_E_INVAL
+    assert L.moe_expert_dedup_ev(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 4, fake, None, fake, need,
+                                 None, None, 2) == _abi.MOE_E_INVAL
+    assert L.moe_kernels_per_call(0) == 1 and L.moe_kernels_per_call(1) == 1
+    assert L.moe_kernels_per_call(5) == _abi.MOE_E_INVAL
     # grouping limits
     assert L.moe_route_group(fake, 129, 2, 8, fake, fake, fake, fake, fake, None) == _abi.MOE_E_INVAL
     assert L.moe_route_group(fake, 4, 9, 8, fake, fake, fake, fake, fake, None) == _abi.MOE_E_INVAL

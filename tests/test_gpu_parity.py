@@ -58,7 +58,8 @@ def test_route_group_configs_and_invalid():
 
 
 def _compare(dl, x, ids, w, what, shared=False, tokens=None, bitwise=True):
-    ys, yd, ue = dl.run(x, ids, w, shared=shared)
+    ys, yd, info = dl.run(x, ids, w, shared=shared)
+    assert info[0] == oracle.union_count(ids, dl.spec.N) and info[1] == 0
     ref = dl.oracle_y(x, ids, w, shared=shared, tokens=tokens)
     sel = slice(None) if tokens is None else tokens
     r1 = assert_close(ys[sel], ref, what + " perslot")
@@ -116,8 +117,8 @@ def test_invalid_ids_skip_slot_and_flag():
     w = np.array([[0.5, 0.5], [0.7, 0.3], [0.6, 0.4]], np.float32)
     x = synth.pass_x(spec, 5, 0, 0, 3)
     say("invalid ids")
-    ys, yd, ue = dl.run(x, ids, w)
-    assert ue[1] == efa._abi.MOE_E_IDS and ue[0] == 5
+    ys, yd, info = dl.run(x, ids, w)
+    assert info[1] == efa._abi.MOE_E_IDS and info[0] == 5
     ids_ok = ids.copy()
     ids_ok[1, 1] = 7
     w_ok = w.copy()
@@ -144,7 +145,7 @@ def test_accumulate_and_determinism():
     w = torch.from_numpy(tr.w).cuda()
     y0 = torch.randn(6, 256, device="cuda")
     y = y0.clone()
-    efa.expert_perslot(dl.dev, xd, ids, w, y=y, accumulate=True)
+    efa.expert_perslot(dl.dev, xd, ids, w, y=y, ws=dl.dev.workspace(6), accumulate=True)
     torch.cuda.synchronize()
     assert torch.equal(y.cpu(), (y0 + torch.from_numpy(a[0]).cuda()).cpu())
 
@@ -196,3 +197,28 @@ def test_mixtral_sampled_tokens():
         x = synth.pass_x(spec, 9, 0, n, n)
         say("mixtral n", n, "tokens", toks)
         _compare(dl, x, ids, w, "mixtral n=%d" % n, tokens=toks)
+
+
+@pytest.mark.parametrize("kind", ["uniform", "correlated"])
+def test_repeated_passes_bitwise_stable(dsv2, kind):
+    """Many back-to-back passes on one workspace: every result bitwise equal to the
+    first, per-slot equal to dedup.  Data handed between workgroups (h, O) that
+    were not yet visible, or counters not reset between calls, would break it."""
+    spec = dsv2.spec
+    tr = routing.make_trace(spec, kind, 256, seed=31, p=0.5)
+    ws = dsv2.dev.workspace(8)
+    info = torch.zeros(3, dtype=torch.int32, device="cuda")
+    for n in (1, 3, 8):
+        ids_h, w_h = routing.window(tr, 7 * n, n)
+        x = to_torch(synth.pass_x(spec, 31, 0, n, n))
+        ids, w = _ids_dev(ids_h), torch.from_numpy(w_h).cuda()
+        say("repeat", kind, "n", n)
+        ref = efa.expert_perslot(dsv2.dev, x, ids, w, ws=ws).clone()
+        outs = []
+        for it in range(40):
+            fn = efa.expert_perslot if it % 2 == 0 else efa.expert_dedup
+            outs.append(fn(dsv2.dev, x, ids, w, ws=ws, info=info).clone())
+        torch.cuda.synchronize()
+        for o in outs:
+            assert torch.equal(o, ref)
+        assert int(info[2].item()) == 0
