@@ -185,9 +185,9 @@ struct Args {
     int32_t accumulate;
 };
 
-template <int NT>
+template <int NB>
 struct Smem {
-    f32x4 red[kWaves][2][NT][64];  // cross-wave reduction of the MFMA accumulators
+    f32x4 red[kWaves][2][NB][64];  // cross-wave reduction of the MFMA accumulators (NB = row blocks x token tiles)
     int32_t ids[MOE_MAX_SLOTS];
     int32_t grp[MOE_MAX_SLOTS];    // slots of this workgroup's unit, increasing
     uint32_t pres[MOE_MAX_EXPERTS / 32];
@@ -199,8 +199,8 @@ struct Smem {
 // number `u` (ids in increasing order).  Also the number U of distinct in-range
 // experts and, when want_status, MOE_E_IDS for ids out of range or repeated within
 // a token.  Leaves e (or -1), g in sm.meta and the slots in sm.grp.
-template <int NT>
-__device__ void group_prologue(const Args& a, Smem<NT>& sm, int u, bool want_status) {
+template <int NB>
+__device__ void group_prologue(const Args& a, Smem<NB>& sm, int u, bool want_status) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nm = a.n * a.m;
     const int nwords = (a.N + 31) >> 5;
@@ -272,12 +272,15 @@ __device__ bool wait_count(const int32_t* p, int target) {
 // ---------------------------------------------------------------------------
 // The fused expert operation.
 // ---------------------------------------------------------------------------
-template <bool BF16, int MODE, int NT, bool KF>
+template <bool BF16, int MODE, int NT, int RB, bool KF>
 __global__ __launch_bounds__(kThreads) void k_expert(Args a) {
     using F = Fmt<BF16>;
-    constexpr int P = NT == 1 ? 8 : (NT == 2 ? 6 : 4);  // ring depth, in steps
-    constexpr int H = P / 2;                            // half ring
-    __shared__ Smem<NT> sm;
+    // ring depth in steps: operand registers per step are (2*RB + NT) for gate/up
+    // and (RB + 2*NT) for down, 4 VGPRs each
+    constexpr int P = (2 * RB + NT) <= 3 ? 8 : ((2 * RB + NT) <= 6 ? 4 : 2);
+    constexpr int H = P / 2;  // half ring
+    constexpr int RT = kTile * RB;  // output rows per item
+    __shared__ Smem<NT * RB> sm;
     __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so step offsets are scalar
@@ -296,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void k_expert(Args a) {
     int e, g;
     const bool want_status = a.info != nullptr && blockIdx.x == 0;
     if (MODE == kDedup || want_status) {
-        group_prologue<NT>(a, sm, MODE == kDedup ? u : 0, want_status);
+        group_prologue<NT * RB>(a, sm, MODE == kDedup ? u : 0, want_status);
         if (want_status && tid == 0) {
             a.info[0] = sm.meta[2];
             a.info[1] = sm.meta[3] ? MOE_E_IDS : MOE_OK;
@@ -315,9 +318,8 @@ __global__ __launch_bounds__(kThreads) void k_expert(Args a) {
     }
 
     if (phase1) {
-        // ======================= gate / up: h for 16 rows of d_ff ==================
+        // ================ gate / up: h for RT rows of d_ff ================
         if (g > 0) {
-            const int row = t * kTile + lr;
             const uint32_t mat = (uint32_t)a.d_ff * a.d * F::kEsize;
             const auto rg = rsrc(a.wg + (size_t)e * mat, mat);
             const auto ru = rsrc(a.wu + (size_t)e * mat, mat);
@@ -327,7 +329,12 @@ __global__ __launch_bounds__(kThreads) void k_expert(Args a) {
             const int s0 = wave * S / kWaves;
             const Steps<BF16, KF> st{s0, (wave + 1) * S / kWaves - s0, a.d, q};
             const int ns = st.ns;
-            const uint32_t lrow = st.lane_base(row < a.d_ff ? (uint32_t)row * a.d * F::kEsize : kOOB);
+            uint32_t lrow[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const int row = t * RT + rb * kTile + lr;
+                lrow[rb] = st.lane_base(row < a.d_ff ? (uint32_t)row * a.d * F::kEsize : kOOB);
+            }
             for (int base = 0; base < g; base += 16 * NT) {
                 uint32_t lx[NT];
 #pragma unroll
@@ -335,18 +342,24 @@ __global__ __launch_bounds__(kThreads) void k_expert(Args a) {
                     const int gi = base + tt * 16 + lr;
                     lx[tt] = st.lane_base(gi < g ? (uint32_t)(sm.grp[gi] / a.m) * a.d * F::kEsize : kOOB);
                 }
-                u32x4 ag[P], au[P], bx[P][NT];
+                u32x4 ag[P][RB], au[P][RB], bx[P][NT];
+                auto issue = [&](int slot, int j) {  // loads of wave step j into ring slot `slot`
+                    const uint32_t so = st.sofs(j);
 #pragma unroll
-                for (int i = 0; i < P; ++i) {
-                    const uint32_t so = st.sofs(i);
-                    ag[i] = bload2<0>(rg, st.vofs(lrow, i), so);
-                    au[i] = bload2<0>(ru, st.vofs(lrow, i), so);
+                    for (int rb = 0; rb < RB; ++rb) {
+                        ag[slot][rb] = bload2<0>(rg, st.vofs(lrow[rb], j), so);
+                        au[slot][rb] = bload2<0>(ru, st.vofs(lrow[rb], j), so);
+                    }
 #pragma unroll
-                    for (int tt = 0; tt < NT; ++tt) bx[i][tt] = bload2<0>(rx, st.vofs(lx[tt], i), so);
-                }
-                f32x4 accg[NT], accu[NT];
+                    for (int tt = 0; tt < NT; ++tt) bx[slot][tt] = bload2<0>(rx, st.vofs(lx[tt], j), so);
+                };
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt) accg[tt] = accu[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int i = 0; i < P; ++i) issue(i, i);
+                f32x4 accg[RB][NT], accu[RB][NT];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt) accg[rb][tt] = accu[rb][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
                 // two halves of the ring: the refill of one half is issued while the
                 // other half's data is consumed, so the wave's load stream never drains
                 for (int s = 0; s < ns; s += P) {
@@ -355,40 +368,37 @@ __global__ __launch_bounds__(kThreads) void k_expert(Args a) {
 #pragma unroll
                         for (int i = hh * H; i < hh * H + H; ++i)
 #pragma unroll
-                            for (int tt = 0; tt < NT; ++tt) {
-                                accg[tt] = F::mma(ag[i], bx[i][tt], accg[tt]);
-                                accu[tt] = F::mma(au[i], bx[i][tt], accu[tt]);
-                            }
+                            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                                for (int tt = 0; tt < NT; ++tt) {
+                                    accg[rb][tt] = F::mma(ag[i][rb], bx[i][tt], accg[rb][tt]);
+                                    accu[rb][tt] = F::mma(au[i][rb], bx[i][tt], accu[rb][tt]);
+                                }
                         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                        for (int i = hh * H; i < hh * H + H; ++i) {
-                            const int j = s + i + P;
-                            const uint32_t so = st.sofs(j);
-                            ag[i] = bload2<0>(rg, st.vofs(lrow, j), so);
-                            au[i] = bload2<0>(ru, st.vofs(lrow, j), so);
-#pragma unroll
-                            for (int tt = 0; tt < NT; ++tt) bx[i][tt] = bload2<0>(rx, st.vofs(lx[tt], j), so);
-                        }
+                        for (int i = hh * H; i < hh * H + H; ++i) issue(i, s + i + P);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt) {
-                    sm.red[wave][0][tt][lane] = accg[tt];
-                    sm.red[wave][1][tt][lane] = accu[tt];
-                }
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt) {
+                        sm.red[wave][0][rb * NT + tt][lane] = accg[rb][tt];
+                        sm.red[wave][1][rb * NT + tt][lane] = accu[rb][tt];
+                    }
                 __syncthreads();
-                if (wave < NT) {  // wave tt finalises token tile tt
-                    const int tt = wave;
-                    f32x4 G = sm.red[0][0][tt][lane], Uu = sm.red[0][1][tt][lane];
+                if (wave < RB * NT) {  // wave w finalises row block w / NT, token tile w % NT
+                    const int rb = wave / NT, tt = wave - rb * NT;
+                    f32x4 G = sm.red[0][0][wave][lane], Uu = sm.red[0][1][wave][lane];
 #pragma unroll
                     for (int w = 1; w < kWaves; ++w) {
-                        G += sm.red[w][0][tt][lane];
-                        Uu += sm.red[w][1][tt][lane];
+                        G += sm.red[w][0][wave][lane];
+                        Uu += sm.red[w][1][wave][lane];
                     }
-                    const int gi = base + tt * 16 + lr;  // output column = lane % 16
-                    const int f0 = t * kTile + 4 * q;    // output rows 4q .. 4q+3
-                    if (gi < g && f0 < a.d_ff) {         // d_ff % 8 == 0: rows f0..f0+3 all valid
+                    const int gi = base + tt * 16 + lr;                // output column = lane % 16
+                    const int f0 = t * RT + rb * kTile + 4 * q;        // output rows f0 .. f0+3
+                    if (gi < g && f0 < a.d_ff) {                       // d_ff % 8 == 0: all 4 rows valid
                         const uint32_t idx = (uint32_t)sm.grp[gi] * a.d_ff + f0;
                         float hv[4];
 #pragma unroll
@@ -417,9 +427,8 @@ __global__ __launch_bounds__(kThreads) void k_expert(Args a) {
         }
         if (tid == 0 && g > 0) atomicAdd(hcnt, 1);  // after the writers' completed stores and the barrier
     } else {
-        // ======================= down: O for 16 rows of d ===========================
+        // ================ down: O for RT rows of d ================
         if (g > 0) {
-            const int row = t * kTile + lr;
             const uint32_t mat = (uint32_t)a.d * a.d_ff * F::kEsize;
             const auto rd = rsrc(a.wd + (size_t)e * mat, mat);
             const uint32_t hbytes = (uint32_t)nm * a.d_ff * F::kEsize;
@@ -430,68 +439,79 @@ __global__ __launch_bounds__(kThreads) void k_expert(Args a) {
             const int s0 = wave * S / kWaves;
             const Steps<BF16, KF> st{s0, (wave + 1) * S / kWaves - s0, a.d_ff, q};
             const int ns = st.ns;
-            const uint32_t lrow = st.lane_base(row < a.d ? (uint32_t)row * a.d_ff * F::kEsize : kOOB);
-            for (int base = 0; base < g; base += 16 * NT) {
-                u32x4 ad[P], bh[P][NT], bl[P][NT];
+            uint32_t lrow[RB];
 #pragma unroll
-                for (int i = 0; i < P; ++i) ad[i] = bload2<0>(rd, st.vofs(lrow, i), st.sofs(i));  // weights first
+            for (int rb = 0; rb < RB; ++rb) {
+                const int row = t * RT + rb * kTile + lr;
+                lrow[rb] = st.lane_base(row < a.d ? (uint32_t)row * a.d_ff * F::kEsize : kOOB);
+            }
+            for (int base = 0; base < g; base += 16 * NT) {
+                u32x4 ad[P][RB], bh[P][NT], bl[P][NT];
+                uint32_t lh[NT];
+                auto issue_a = [&](int slot, int j) {
+                    const uint32_t so = st.sofs(j);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) ad[slot][rb] = bload2<0>(rd, st.vofs(lrow[rb], j), so);
+                };
+                auto issue_b = [&](int slot, int j) {
+                    const uint32_t so = st.sofs(j);
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt) {
+                        bh[slot][tt] = bload2<kSc1>(rh, st.vofs(lh[tt], j), so);
+                        if (BF16) bl[slot][tt] = bload2<kSc1>(rl, st.vofs(lh[tt], j), so);
+                    }
+                };
+#pragma unroll
+                for (int i = 0; i < P; ++i) issue_a(i, i);  // weights first
                 if (base == 0) {
                     if (tid == 0 && !wait_count(hcnt, a.T1) && a.info) a.info[2] = MOE_E_HIP;
                     __syncthreads();  // h loads (sc1) below are issued after the count was seen
                 }
-                uint32_t lh[NT];
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) {
                     const int gi = base + tt * 16 + lr;
                     lh[tt] = st.lane_base(gi < g ? (uint32_t)sm.grp[gi] * a.d_ff * F::kEsize : kOOB);
                 }
 #pragma unroll
-                for (int i = 0; i < P; ++i) {
-                    const uint32_t so = st.sofs(i);
+                for (int i = 0; i < P; ++i) issue_b(i, i);
+                f32x4 acc[RB][NT];
 #pragma unroll
-                    for (int tt = 0; tt < NT; ++tt) {
-                        bh[i][tt] = bload2<kSc1>(rh, st.vofs(lh[tt], i), so);
-                        if (BF16) bl[i][tt] = bload2<kSc1>(rl, st.vofs(lh[tt], i), so);
-                    }
-                }
-                f32x4 acc[NT];
+                for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int tt = 0; tt < NT; ++tt) acc[rb][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
                 for (int s = 0; s < ns; s += P) {
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
                         for (int i = hh * H; i < hh * H + H; ++i)
 #pragma unroll
-                            for (int tt = 0; tt < NT; ++tt) {
-                                acc[tt] = F::mma(ad[i], bh[i][tt], acc[tt]);
-                                if (BF16) acc[tt] = F::mma(ad[i], bl[i][tt], acc[tt]);
-                            }
+                            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                                for (int tt = 0; tt < NT; ++tt) {
+                                    acc[rb][tt] = F::mma(ad[i][rb], bh[i][tt], acc[rb][tt]);
+                                    if (BF16) acc[rb][tt] = F::mma(ad[i][rb], bl[i][tt], acc[rb][tt]);
+                                }
                         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                         for (int i = hh * H; i < hh * H + H; ++i) {
-                            const int j = s + i + P;
-                            const uint32_t so = st.sofs(j);
-                            ad[i] = bload2<0>(rd, st.vofs(lrow, j), so);
-#pragma unroll
-                            for (int tt = 0; tt < NT; ++tt) {
-                                bh[i][tt] = bload2<kSc1>(rh, st.vofs(lh[tt], j), so);
-                                if (BF16) bl[i][tt] = bload2<kSc1>(rl, st.vofs(lh[tt], j), so);
-                            }
+                            issue_a(i, s + i + P);
+                            issue_b(i, s + i + P);
                         }
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt) sm.red[wave][0][tt][lane] = acc[tt];
-                __syncthreads();
-                if (wave < NT) {
-                    const int tt = wave;
-                    f32x4 v = sm.red[0][0][tt][lane];
+                for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                    for (int w = 1; w < kWaves; ++w) v += sm.red[w][0][tt][lane];
+                    for (int tt = 0; tt < NT; ++tt) sm.red[wave][0][rb * NT + tt][lane] = acc[rb][tt];
+                __syncthreads();
+                if (wave < RB * NT) {
+                    const int rb = wave / NT, tt = wave - rb * NT;
+                    f32x4 v = sm.red[0][0][wave][lane];
+#pragma unroll
+                    for (int w = 1; w < kWaves; ++w) v += sm.red[w][0][wave][lane];
                     const int gi = base + tt * 16 + lr;
-                    const int i0 = t * kTile + 4 * q;
+                    const int i0 = t * RT + rb * kTile + 4 * q;
                     if (gi < g && i0 < a.d)  // d % 8 == 0: rows i0..i0+3 all valid
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro,
                                                                ((uint32_t)sm.grp[gi] * a.d + i0) * 4, 0, kSc1);
@@ -514,8 +534,8 @@ __global__ __launch_bounds__(kThreads) void k_expert(Args a) {
         }
         __syncthreads();  // O loads (sc1) below are issued after the last arrival was seen
         if (s_last) {
-            const int i0 = t * kTile;
-            const int rows = min(kTile, a.d - i0);
+            const int i0 = t * RT;
+            const int rows = min(RT, a.d - i0);
             for (int o = tid; o < a.n * rows; o += kThreads) {
                 const int tok = o / rows, i = i0 + (o - tok * rows);
                 float acc = 0.f;
@@ -531,7 +551,6 @@ __global__ __launch_bounds__(kThreads) void k_expert(Args a) {
             }
         }
     }
-
 }
 
 // ---------------------------------------------------------------------------
@@ -645,7 +664,7 @@ int check_desc(const moe_layer_desc* d, int32_t n) {
 }
 
 struct Plan {
-    int units, T1, T2, nt;
+    int units, T1, T2, nt, rb;
     size_t h_off, o_off, sync_off, total;
 };
 
@@ -653,9 +672,10 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     Plan p;
     const int nm = n * d->m;
     p.units = kind == MOE_KIND_SLOT ? nm : (nm < d->N ? nm : d->N);
-    p.T1 = (d->d_ff + kTile - 1) / kTile;
-    p.T2 = (d->d_model + kTile - 1) / kTile;
     p.nt = kind == MOE_KIND_SLOT ? 1 : (n <= 16 ? 1 : (n <= 32 ? 2 : 4));
+    p.rb = p.nt == 4 ? 1 : 2;  // rows per item = 16 * rb; row blocks x token tiles <= 4
+    p.T1 = (d->d_ff + kTile * p.rb - 1) / (kTile * p.rb);
+    p.T2 = (d->d_model + kTile * p.rb - 1) / (kTile * p.rb);
     p.sync_off = 0;
     p.h_off = (size_t)kSyncWords * 4;
     p.o_off = p.h_off + align_up((size_t)nm * d->d_ff * 4);
@@ -663,13 +683,13 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     return p;
 }
 
-template <bool BF16, int MODE, int NT>
+template <bool BF16, int MODE, int NT, int RB>
 void launch(const Args& args, int grid, hipStream_t st) {
     constexpr int step = Fmt<BF16>::kStep;
     if (args.d % step == 0 && args.d_ff % step == 0)
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, true>), dim3(grid), dim3(kThreads), 0, st, args);
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true>), dim3(grid), dim3(kThreads), 0, st, args);
     else
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, false>), dim3(grid), dim3(kThreads), 0, st, args);
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false>), dim3(grid), dim3(kThreads), 0, st, args);
 }
 
 template <int MODE>
@@ -718,13 +738,13 @@ int run_expert(const moe_layer_desc* d, const moe_layer_weights* W, const void* 
     if (events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(events[0]), st);
     const bool bf = d->dtype == MOE_BF16;
     if (bf) {
-        if (p.nt == 1) launch<true, MODE, 1>(args, grid, st);
-        else if (p.nt == 2) launch<true, MODE, 2>(args, grid, st);
-        else launch<true, MODE, 4>(args, grid, st);
+        if (p.nt == 1) launch<true, MODE, 1, 2>(args, grid, st);
+        else if (p.nt == 2) launch<true, MODE, 2, 2>(args, grid, st);
+        else launch<true, MODE, 4, 1>(args, grid, st);
     } else {
-        if (p.nt == 1) launch<false, MODE, 1>(args, grid, st);
-        else if (p.nt == 2) launch<false, MODE, 2>(args, grid, st);
-        else launch<false, MODE, 4>(args, grid, st);
+        if (p.nt == 1) launch<false, MODE, 1, 2>(args, grid, st);
+        else if (p.nt == 2) launch<false, MODE, 2, 2>(args, grid, st);
+        else launch<false, MODE, 4, 1>(args, grid, st);
     }
     if (events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(events[1]), st);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
