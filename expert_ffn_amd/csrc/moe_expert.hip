@@ -64,9 +64,13 @@ constexpr int kSpinLimit = 1 << 17;          // bounded wait on a counter (~0.2 
 //   line u,  word 0   h-ready count of unit u: gate/up items of u that wrote h
 //   line u,  word 1   down items of unit u that finished reading h
 //   line 256 + t      arrivals of units on down row tile t
+//   line 1280 + c     contributions to split gate/up tile c
 constexpr int kLine = 32;
 constexpr int kMaxDownTiles = 1024;  // d_model <= 16384
-constexpr int kSyncWords = kLine * (MOE_MAX_SLOTS + kMaxDownTiles);
+constexpr int kCUs = 256;            // compute units: the gate/up split balances work over them
+constexpr int kMaxSplitTiles = 2 * kCUs;
+constexpr int kMaxContrib = 3;       // work groups sharing one split gate/up tile
+constexpr int kSyncWords = kLine * (MOE_MAX_SLOTS + kMaxDownTiles + kMaxSplitTiles);
 
 // byte offset base + k, or the out-of-range offset when either part is out of range
 __device__ __forceinline__ uint32_t cat(uint32_t base, uint32_t k) {
@@ -76,6 +80,8 @@ __device__ __forceinline__ uint32_t cat(uint32_t base, uint32_t k) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
 }
+
+__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -164,6 +170,9 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_floa
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// a value that is the same in every lane, kept in a scalar register
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 __device__ __forceinline__ int atomic_load_agent(const int32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -183,6 +192,10 @@ struct Args {
     int32_t n, m, N, d, d_ff;
     int32_t units, T1, T2;
     int32_t accumulate;
+    int32_t gl;          // down items in register mode: tokens of h staged in LDS at a time
+    int32_t g1;          // gate/up work groups (they take the first g1 block ids)
+    int32_t S1;          // K steps of one gate/up row tile
+    float* part;         // split gate/up tiles: partial sums [kMaxContrib][nm][d_ff][gate, up]
 };
 
 template <int NB>
@@ -193,6 +206,7 @@ struct Smem {
     uint32_t pres[MOE_MAX_EXPERTS / 32];
     int32_t wsum[kWaves];
     int32_t meta[4];               // e, g, U, flag
+    int32_t fin;                   // this work group finalises a split gate/up tile
 };
 
 // Stable grouping of the pass's slots by expert, in LDS, for distinct expert
@@ -270,164 +284,292 @@ __device__ bool wait_count(const int32_t* p, int target) {
 }
 
 // ---------------------------------------------------------------------------
+// Gate/up products of one segment of a row tile: rows t*RT .. t*RT+RT-1 of d_ff
+// for the unit (expert e, slots sm.grp[0..g)), over K steps k0 .. k1-1 of the
+// contraction, split over the four waves.  A segment that covers all of K
+// (nc == 1) finalises h = silu(gate) * up at once.  Otherwise the tile is shared
+// by nc consecutive work groups, contributor j = 0 .. nc-1 in K order: the first
+// nc-1 store their partial sums and count in; the last (the finaliser, highest
+// work-group id, so every work group it waits for was dispatched before it and
+// never waits on a higher id) waits for the count, adds the partials in
+// contributor order and then its own, and finalises h.  Returns true in the work
+// group that finalised the tile.
+// ---------------------------------------------------------------------------
+template <bool BF16, int NT, int RB, bool KF, int P>
+__device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e, int g, int t, int k0, int k1,
+                                        int tile, int nc, int j) {
+    using F = Fmt<BF16>;
+    constexpr int H = P / 2;        // half ring
+    constexpr int RT = kTile * RB;  // output rows of a tile
+    // lane-dependent values are formed afresh for every segment (an opaque copy of
+    // the thread id), not hoisted out of the caller's loop over segments, where they
+    // would hold registers through the load ring
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, q = lane >> 4;
+    const int nm = a.n * a.m;
+    const uint32_t mat = (uint32_t)a.d_ff * a.d * F::kEsize;
+    const auto rg = rsrc(a.wg + (size_t)e * mat, mat);
+    const auto ru = rsrc(a.wu + (size_t)e * mat, mat);
+    const auto rx = rsrc(a.x, (uint32_t)(a.n * a.d * F::kEsize));
+    int32_t* tc = a.sync + kLine * (MOE_MAX_SLOTS + kMaxDownTiles + tile);  // split tile: partials stored
+    const int len = k1 - k0;
+    const int s0 = k0 + wave * len / kWaves;
+    const Steps<BF16, KF> st{s0, k0 + (wave + 1) * len / kWaves - s0, a.d, q};
+    const int ns = st.ns;
+    // h = silu(G) * U for rows f0 .. f0+3 of slot `slot` (bf16: hi and lo halves)
+    auto store_h = [&](f32x4 G, f32x4 Uu, int slot, int f0) {
+        const auto rhw = rsrc(a.h, (uint32_t)nm * a.d_ff * 4);  // h region: hi+lo bf16 or fp32
+        const uint32_t idx = (uint32_t)slot * a.d_ff + f0;
+        float hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = silu(G[i]) * Uu[i];
+        if (BF16) {
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                hi[i] = bf16_rne(hv[i]);
+                lo[i] = bf16_rne(hv[i] - bf16_to_f32(hi[i]));
+            }
+            const uint32_t half = (uint32_t)nm * a.d_ff * 2;  // bytes of the hi half
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)}, rhw, idx * 2,
+                                                  0, kSc1);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)}, rhw,
+                                                  half + idx * 2, 0, kSc1);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{hv[0], hv[1], hv[2], hv[3]}), rhw,
+                                                   idx * 4, 0, kSc1);
+        }
+    };
+    uint32_t lrow[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int row = t * RT + rb * kTile + lr;
+        lrow[rb] = st.lane_base(row < a.d_ff ? (uint32_t)row * a.d * F::kEsize : kOOB);
+    }
+    for (int base = 0; base < g; base += 16 * NT) {
+        uint32_t lx[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const int gi = base + tt * 16 + lr;
+            lx[tt] = st.lane_base(gi < g ? (uint32_t)(sm.grp[gi] / a.m) * a.d * F::kEsize : kOOB);
+        }
+        u32x4 ag[P][RB], au[P][RB], bx[P][NT];
+        auto issue = [&](int slot, int j) {  // loads of wave step j into ring slot `slot`
+            const uint32_t so = st.sofs(j);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                ag[slot][rb] = bload2<0>(rg, st.vofs(lrow[rb], j), so);
+                au[slot][rb] = bload2<0>(ru, st.vofs(lrow[rb], j), so);
+            }
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) bx[slot][tt] = bload2<0>(rx, st.vofs(lx[tt], j), so);
+        };
+#pragma unroll
+        for (int i = 0; i < P; ++i) issue(i, i);
+        f32x4 accg[RB][NT], accu[RB][NT];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) accg[rb][tt] = accu[rb][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // two halves of the ring: the refill of one half is issued while the
+        // other half's data is consumed, so the wave's load stream never drains
+        for (int s = 0; s < ns; s += P) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                for (int i = hh * H; i < hh * H + H; ++i)
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                        for (int tt = 0; tt < NT; ++tt) {
+                            accg[rb][tt] = F::mma(ag[i][rb], bx[i][tt], accg[rb][tt]);
+                            accu[rb][tt] = F::mma(au[i][rb], bx[i][tt], accu[rb][tt]);
+                        }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = hh * H; i < hh * H + H; ++i) issue(i, s + i + P);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                sm.red[wave][0][rb * NT + tt][lane] = accg[rb][tt];
+                sm.red[wave][1][rb * NT + tt][lane] = accu[rb][tt];
+            }
+        // the finaliser of a split tile waits (bounded) until the other nc-1
+        // contributors, all of lower work-group id, have stored their partials
+        if (base == 0 && nc > 1 && j == nc - 1 && tid == 0 && !wait_count(tc, nc - 1) && a.info)
+            a.info[2] = MOE_E_HIP;
+        __syncthreads();  // partial loads (sc1) below are issued after the count was seen
+        if (wave < RB * NT) {  // wave w finalises row block w / NT, token tile w % NT
+            const int rb = wave / NT, tt = wave - rb * NT;
+            f32x4 G = sm.red[0][0][wave][lane], Uu = sm.red[0][1][wave][lane];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) {
+                G += sm.red[w][0][wave][lane];
+                Uu += sm.red[w][1][wave][lane];
+            }
+            const int gi = base + tt * 16 + lr;                // output column = lane % 16
+            const int f0 = t * RT + rb * kTile + 4 * q;        // output rows f0 .. f0+3
+            if (gi < g && f0 < a.d_ff) {                       // d_ff % 8 == 0: all 4 rows valid
+                const int slot = sm.grp[gi];
+                if (nc == 1) {
+                    store_h(G, Uu, slot, f0);
+                } else {
+                    // partial of contributor jj at jj*pstride + pb: (gate, up) pairs of rows f0 .. f0+3
+                    const auto rp = rsrc(a.part, (uint32_t)kMaxContrib * nm * a.d_ff * 8);
+                    const uint32_t pstride = (uint32_t)nm * a.d_ff * 8;
+                    const uint32_t pb = ((uint32_t)slot * a.d_ff + f0) * 8;
+                    if (j < nc - 1) {
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            u32x4{__float_as_uint(G[0]), __float_as_uint(Uu[0]), __float_as_uint(G[1]),
+                                  __float_as_uint(Uu[1])},
+                            rp, j * pstride + pb, 0, kSc1);
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            u32x4{__float_as_uint(G[2]), __float_as_uint(Uu[2]), __float_as_uint(G[3]),
+                                  __float_as_uint(Uu[3])},
+                            rp, j * pstride + pb + 16, 0, kSc1);
+                    } else {
+                        // the others' partials, all loads in flight, added in contributor
+                        // order, then this work group's own
+                        u32x4 pv[kMaxContrib - 1][2];
+#pragma unroll
+                        for (int jj = 0; jj < kMaxContrib - 1; ++jj) {
+                            pv[jj][0] = bload_sc1(rp, jj < j ? jj * pstride + pb : kOOB);
+                            pv[jj][1] = bload_sc1(rp, jj < j ? jj * pstride + pb + 16 : kOOB);
+                        }
+                        f32x4 Gs = f32x4{0.f, 0.f, 0.f, 0.f}, Us = Gs;
+#pragma unroll
+                        for (int jj = 0; jj < kMaxContrib - 1; ++jj) {
+                            if (jj < j) {
+                                Gs += f32x4{__uint_as_float(pv[jj][0].x), __uint_as_float(pv[jj][0].z),
+                                            __uint_as_float(pv[jj][1].x), __uint_as_float(pv[jj][1].z)};
+                                Us += f32x4{__uint_as_float(pv[jj][0].y), __uint_as_float(pv[jj][0].w),
+                                            __uint_as_float(pv[jj][1].y), __uint_as_float(pv[jj][1].w)};
+                            }
+                        }
+                        store_h(Gs + G, Us + Uu, slot, f0);
+                    }
+                }
+            }
+            stores_complete();
+        }
+        __syncthreads();
+    }
+    if (nc == 1) return true;
+    if (j < nc - 1) {
+        if (tid == 0) atomicAdd(tc, 1);  // after the writers' completed stores and the barrier
+        return false;
+    }
+    if (tid == 0) __hip_atomic_store(tc, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // all nc-1 were counted
+    return true;
+}
+
+// ---------------------------------------------------------------------------
 // The fused expert operation.
 // ---------------------------------------------------------------------------
-template <bool BF16, int MODE, int NT, int RB, bool KF>
-__global__ __launch_bounds__(kThreads) void k_expert(Args a) {
+// Down items hold all of their W_down rows in registers (DPF) when a wave's share
+// of the contraction is at most kPF steps.
+constexpr int kPF = 12;
+constexpr int kSL = 4;  // register mode: h staging loads in flight per thread
+
+// The per-slot kernel holds its registers to 4 waves per SIMD, so that a small
+// pass's gate/up and down work groups are all resident at once.
+template <bool BF16, int MODE, int NT, int RB, bool KF, bool DPF>
+__global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(Args a) {
     using F = Fmt<BF16>;
     // ring depth in steps: operand registers per step are (2*RB + NT) for gate/up
     // and (RB + 2*NT) for down, 4 VGPRs each
     constexpr int P = (2 * RB + NT) <= 3 ? 8 : ((2 * RB + NT) <= 6 ? 4 : 2);
     constexpr int H = P / 2;  // half ring
-    constexpr int RT = kTile * RB;  // output rows per item
+    // down items: one row block in register mode (the W_down rows a wave holds),
+    // else RB like the gate/up items
+    constexpr int RB2 = DPF ? 1 : RB;
+    constexpr int RT2 = kTile * RB2;
     __shared__ Smem<NT * RB> sm;
     __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so step offsets are scalar
     const int lr = lane & 15, q = lane >> 4;
     const int nm = a.n * a.m;
-    const int A1 = a.units * a.T1;
-    const bool phase1 = (int)blockIdx.x < A1;
-    const int item = phase1 ? (int)blockIdx.x : (int)blockIdx.x - A1;
-    const int T = phase1 ? a.T1 : a.T2;
-    const int u = item / T, t = item - u * T;
-    int32_t* hcnt = a.sync + kLine * u;      // this unit's h-ready count
-    int32_t* dcnt = hcnt + 1;                // this unit's finished down items
-    int32_t* ocnt = a.sync + kLine * (MOE_MAX_SLOTS + t);  // arrivals on this down tile (phase 2)
-
-    // ---- the unit: expert e and its slots sm.grp[0..g) ----
-    int e, g;
+    const bool phase1 = (int)blockIdx.x < a.g1;
     const bool want_status = a.info != nullptr && blockIdx.x == 0;
-    if (MODE == kDedup || want_status) {
-        group_prologue<NT * RB>(a, sm, MODE == kDedup ? u : 0, want_status);
-        if (want_status && tid == 0) {
-            a.info[0] = sm.meta[2];
-            a.info[1] = sm.meta[3] ? MOE_E_IDS : MOE_OK;
-            a.info[2] = MOE_OK;  // a bounded wait that expires later overwrites this
+
+    // The unit u: expert e and its slots sm.grp[0..g).  `status`: also report U and
+    // the ids' status (work group 0).
+    auto resolve = [&](int u, bool status, int& e, int& g) {
+        if (MODE == kDedup || status) {
+            group_prologue<NT * RB>(a, sm, MODE == kDedup ? u : 0, status);
+            if (status && tid == 0) {
+                a.info[0] = sm.meta[2];
+                a.info[1] = sm.meta[3] ? MOE_E_IDS : MOE_OK;
+                a.info[2] = MOE_OK;  // a bounded wait that expires later overwrites this
+            }
         }
-    }
-    if (MODE == kDedup) {
-        e = sm.meta[0];
-        g = sm.meta[1];
-    } else {
-        const int id = a.ids[u];
-        e = (id >= 0 && id < a.N) ? id : -1;
-        g = e >= 0 ? 1 : 0;
-        if (tid == 0) sm.grp[0] = u;
-        __syncthreads();
-    }
+        if (MODE == kDedup) {
+            e = uni(sm.meta[0]);
+            g = uni(sm.meta[1]);
+        } else {
+            const int id = uni(a.ids[u]);
+            e = (id >= 0 && id < a.N) ? id : -1;
+            g = e >= 0 ? 1 : 0;
+            if (tid == 0) sm.grp[0] = u;
+            __syncthreads();
+        }
+    };
 
     if (phase1) {
-        // ================ gate / up: h for RT rows of d_ff ================
-        if (g > 0) {
-            const uint32_t mat = (uint32_t)a.d_ff * a.d * F::kEsize;
-            const auto rg = rsrc(a.wg + (size_t)e * mat, mat);
-            const auto ru = rsrc(a.wu + (size_t)e * mat, mat);
-            const auto rx = rsrc(a.x, (uint32_t)(a.n * a.d * F::kEsize));
-            const auto rhw = rsrc(a.h, (uint32_t)nm * a.d_ff * 4);  // h region: hi+lo bf16 or fp32
-            const int S = (a.d + F::kStep - 1) / F::kStep;
-            const int s0 = wave * S / kWaves;
-            const Steps<BF16, KF> st{s0, (wave + 1) * S / kWaves - s0, a.d, q};
-            const int ns = st.ns;
-            uint32_t lrow[RB];
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const int row = t * RT + rb * kTile + lr;
-                lrow[rb] = st.lane_base(row < a.d_ff ? (uint32_t)row * a.d * F::kEsize : kOOB);
+        // ================ gate / up: h for RT rows of d_ff per tile ================
+        // The gate/up work, (unit, row tile, K step) in that order, is cut into g1
+        // equal contiguous shares, one per work group; a tile cut between work
+        // groups is a split tile (see gate_up).
+        // Without a split, work group wi holds tile wi whole.  With one, the
+        // products below stay under 2^31: at most kMaxSplitTiles tiles and
+        // g1 <= kMaxSplitTiles.
+        const int tiles = a.units * a.T1;
+        const bool split = a.g1 != tiles;
+        const int ltot = tiles * a.S1;
+        const int wi = blockIdx.x;
+        // (integer divisions run on the vector unit: readfirstlane keeps the
+        // work-group-uniform values in scalar registers)
+        // The segments run last to first: a work group's last segment is the head
+        // of a split tile (it contributes without waiting) and its first is the
+        // tail of one (it finalises, waiting on lower work-group ids).  In this
+        // order no wait depends on another wait.
+        const int lbeg = uni(split ? wi * ltot / a.g1 : wi * a.S1);
+        int cur = -1, e = -1, g = 0;
+        for (int L = uni(split ? (wi + 1) * ltot / a.g1 : (wi + 1) * a.S1); L > lbeg;) {
+            const int tile = uni((L - 1) / a.S1);
+            const int k1 = L - tile * a.S1;
+            const int k0 = max(0, lbeg - tile * a.S1);
+            L = tile * a.S1 + k0;
+            const int u = uni(tile / a.T1), t = tile - u * a.T1;
+            if (u != cur) {
+                resolve(u, want_status && cur < 0, e, g);
+                cur = u;
             }
-            for (int base = 0; base < g; base += 16 * NT) {
-                uint32_t lx[NT];
-#pragma unroll
-                for (int tt = 0; tt < NT; ++tt) {
-                    const int gi = base + tt * 16 + lr;
-                    lx[tt] = st.lane_base(gi < g ? (uint32_t)(sm.grp[gi] / a.m) * a.d * F::kEsize : kOOB);
-                }
-                u32x4 ag[P][RB], au[P][RB], bx[P][NT];
-                auto issue = [&](int slot, int j) {  // loads of wave step j into ring slot `slot`
-                    const uint32_t so = st.sofs(j);
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) {
-                        ag[slot][rb] = bload2<0>(rg, st.vofs(lrow[rb], j), so);
-                        au[slot][rb] = bload2<0>(ru, st.vofs(lrow[rb], j), so);
-                    }
-#pragma unroll
-                    for (int tt = 0; tt < NT; ++tt) bx[slot][tt] = bload2<0>(rx, st.vofs(lx[tt], j), so);
-                };
-#pragma unroll
-                for (int i = 0; i < P; ++i) issue(i, i);
-                f32x4 accg[RB][NT], accu[RB][NT];
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int tt = 0; tt < NT; ++tt) accg[rb][tt] = accu[rb][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                // two halves of the ring: the refill of one half is issued while the
-                // other half's data is consumed, so the wave's load stream never drains
-                for (int s = 0; s < ns; s += P) {
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-                        for (int i = hh * H; i < hh * H + H; ++i)
-#pragma unroll
-                            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                                for (int tt = 0; tt < NT; ++tt) {
-                                    accg[rb][tt] = F::mma(ag[i][rb], bx[i][tt], accg[rb][tt]);
-                                    accu[rb][tt] = F::mma(au[i][rb], bx[i][tt], accu[rb][tt]);
-                                }
-                        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                        for (int i = hh * H; i < hh * H + H; ++i) issue(i, s + i + P);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int tt = 0; tt < NT; ++tt) {
-                        sm.red[wave][0][rb * NT + tt][lane] = accg[rb][tt];
-                        sm.red[wave][1][rb * NT + tt][lane] = accu[rb][tt];
-                    }
-                __syncthreads();
-                if (wave < RB * NT) {  // wave w finalises row block w / NT, token tile w % NT
-                    const int rb = wave / NT, tt = wave - rb * NT;
-                    f32x4 G = sm.red[0][0][wave][lane], Uu = sm.red[0][1][wave][lane];
-#pragma unroll
-                    for (int w = 1; w < kWaves; ++w) {
-                        G += sm.red[w][0][wave][lane];
-                        Uu += sm.red[w][1][wave][lane];
-                    }
-                    const int gi = base + tt * 16 + lr;                // output column = lane % 16
-                    const int f0 = t * RT + rb * kTile + 4 * q;        // output rows f0 .. f0+3
-                    if (gi < g && f0 < a.d_ff) {                       // d_ff % 8 == 0: all 4 rows valid
-                        const uint32_t idx = (uint32_t)sm.grp[gi] * a.d_ff + f0;
-                        float hv[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) hv[i] = silu(G[i]) * Uu[i];
-                        if (BF16) {
-                            uint32_t hi[4], lo[4];
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                hi[i] = bf16_rne(hv[i]);
-                                lo[i] = bf16_rne(hv[i] - bf16_to_f32(hi[i]));
-                            }
-                            const uint32_t half = (uint32_t)nm * a.d_ff * 2;  // bytes of the hi half
-                            __builtin_amdgcn_raw_buffer_store_b64(u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)},
-                                                                  rhw, idx * 2, 0, kSc1);
-                            __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)},
-                                                                  rhw, half + idx * 2, 0, kSc1);
-                        } else {
-                            __builtin_amdgcn_raw_buffer_store_b128(
-                                __builtin_bit_cast(u32x4, f32x4{hv[0], hv[1], hv[2], hv[3]}), rhw, idx * 4, 0, kSc1);
-                        }
-                    }
-                    stores_complete();
-                }
-                __syncthreads();
-            }
+            if (g == 0) continue;
+            // work groups whose shares meet this tile: first .. last
+            const int first = uni(split ? ((tile * a.S1 + 1) * a.g1 - 1) / ltot : wi);
+            const int last = uni(split ? ((tile * a.S1 + a.S1) * a.g1 - 1) / ltot : wi);
+            const bool fin = gate_up<BF16, NT, RB, KF, P>(a, sm, e, g, t, k0, k1, tile, last - first + 1, wi - first);
+            if (tid == 0 && fin) atomicAdd(a.sync + kLine * u, 1);  // h-ready count of unit u
         }
-        if (tid == 0 && g > 0) atomicAdd(hcnt, 1);  // after the writers' completed stores and the barrier
+        if (want_status && cur < 0) resolve(0, true, e, g);  // an empty share still reports the status
     } else {
-        // ================ down: O for RT rows of d ================
+        const int item = (int)blockIdx.x - a.g1;
+        const int u = item / a.T2, t = item - u * a.T2;
+        int32_t* hcnt = a.sync + kLine * u;      // this unit's h-ready count
+        int32_t* dcnt = hcnt + 1;                // this unit's finished down items
+        int32_t* ocnt = a.sync + kLine * (MOE_MAX_SLOTS + t);  // arrivals on this down tile
+        int e, g;
+        resolve(u, false, e, g);
+        // ================ down: O for RT2 rows of d ================
         if (g > 0) {
             const uint32_t mat = (uint32_t)a.d * a.d_ff * F::kEsize;
             const auto rd = rsrc(a.wd + (size_t)e * mat, mat);
@@ -439,19 +581,101 @@ __global__ __launch_bounds__(kThreads) void k_expert(Args a) {
             const int s0 = wave * S / kWaves;
             const Steps<BF16, KF> st{s0, (wave + 1) * S / kWaves - s0, a.d_ff, q};
             const int ns = st.ns;
-            uint32_t lrow[RB];
+            uint32_t lrow[RB2];
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const int row = t * RT + rb * kTile + lr;
+            for (int rb = 0; rb < RB2; ++rb) {
+                const int row = t * RT2 + rb * kTile + lr;
                 lrow[rb] = st.lane_base(row < a.d ? (uint32_t)row * a.d_ff * F::kEsize : kOOB);
             }
+            if constexpr (DPF) {
+                // All of this wave's W_down rows go to registers before the wait, so
+                // they stream from HBM while gate/up items still run.  After the
+                // wait, h is staged in LDS `gl` tokens at a time (one cooperative
+                // sc1 load per chunk) and the products run from registers and LDS,
+                // for any group size with one read of the weights.
+                extern __shared__ __align__(16) char hs[];  // [gl][hi row, lo row], padded rows
+                u32x4 pa[kPF][RB2];
+#pragma unroll
+                for (int i = 0; i < kPF; ++i) {
+                    const uint32_t so = st.sofs(i);
+#pragma unroll
+                    for (int rb = 0; rb < RB2; ++rb) pa[i][rb] = bload2<0>(rd, st.vofs(lrow[rb], i), so);
+                }
+                if (tid == 0 && !wait_count(hcnt, a.T1) && a.info) a.info[2] = MOE_E_HIP;
+                __syncthreads();  // h loads (sc1) below are issued after the count was seen
+                const auto rhl = rsrc(a.h, BF16 ? 2 * hbytes : hbytes);  // hi half, then lo half
+                const int rowb = a.d_ff * F::kEsize + 16;      // padded LDS row
+                const int tokb = BF16 ? 2 * rowb : rowb;
+                const int per_row = a.d_ff * F::kEsize / 16;   // 16-byte chunks of an h row
+                for (int cb = 0; cb < g; cb += a.gl) {
+                    const int gc = min(a.gl, g - cb);
+                    const int nrows = BF16 ? 2 * gc : gc;
+                    // kSL loads per thread in flight, then their LDS writes
+                    for (int c0 = 0; c0 < nrows * per_row; c0 += kSL * kThreads) {
+                        u32x4 v[kSL];
+                        int dst[kSL];
+#pragma unroll
+                        for (int j = 0; j < kSL; ++j) {
+                            const int c = c0 + j * kThreads + tid;
+                            uint32_t off = kOOB;
+                            dst[j] = -1;
+                            if (c < nrows * per_row) {
+                                const int r = c / per_row, k16 = c - r * per_row;
+                                const int tok = BF16 ? (r >> 1) : r, half = BF16 ? (r & 1) : 0;
+                                off = (uint32_t)half * hbytes + (uint32_t)sm.grp[cb + tok] * a.d_ff * F::kEsize + k16 * 16;
+                                dst[j] = tok * tokb + half * rowb + k16 * 16;
+                            }
+                            v[j] = bload2<kSc1>(rhl, off, 0);
+                        }
+#pragma unroll
+                        for (int j = 0; j < kSL; ++j)
+                            if (dst[j] >= 0) *reinterpret_cast<u32x4*>(hs + dst[j]) = v[j];
+                    }
+                    __syncthreads();
+                    const bool col_ok = lr < gc;
+                    const char* bp = hs + (col_ok ? lr : 0) * tokb;  // this lane's token row
+                    f32x4 acc[RB2];
+#pragma unroll
+                    for (int rb = 0; rb < RB2; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < kPF; ++i) {
+                        if (i < ns) {
+                            const int k = (s0 + i) * F::kStep + q * F::kPer;
+                            const bool ok = col_ok && k < a.d_ff;
+                            const u32x4 bhv = ok ? *reinterpret_cast<const u32x4*>(bp + k * F::kEsize) : zero4();
+                            u32x4 blv = zero4();
+                            if (BF16 && ok) blv = *reinterpret_cast<const u32x4*>(bp + rowb + k * F::kEsize);
+#pragma unroll
+                            for (int rb = 0; rb < RB2; ++rb) {
+                                acc[rb] = F::mma(pa[i][rb], bhv, acc[rb]);
+                                if (BF16) acc[rb] = F::mma(pa[i][rb], blv, acc[rb]);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int rb = 0; rb < RB2; ++rb) sm.red[wave][0][rb][lane] = acc[rb];
+                    __syncthreads();
+                    if (wave < RB2) {
+                        const int rb = wave;
+                        f32x4 v = sm.red[0][0][rb][lane];
+#pragma unroll
+                        for (int w = 1; w < kWaves; ++w) v += sm.red[w][0][rb][lane];
+                        const int i0 = t * RT2 + rb * kTile + 4 * q;
+                        if (col_ok && i0 < a.d)  // d % 8 == 0: rows i0..i0+3 all valid
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro,
+                                                                   ((uint32_t)sm.grp[cb + lr] * a.d + i0) * 4, 0, kSc1);
+                        stores_complete();
+                    }
+                    __syncthreads();
+                }
+            } else
             for (int base = 0; base < g; base += 16 * NT) {
-                u32x4 ad[P][RB], bh[P][NT], bl[P][NT];
+                u32x4 ad[P][RB2], bh[P][NT], bl[P][NT];
                 uint32_t lh[NT];
                 auto issue_a = [&](int slot, int j) {
                     const uint32_t so = st.sofs(j);
 #pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) ad[slot][rb] = bload2<0>(rd, st.vofs(lrow[rb], j), so);
+                    for (int rb = 0; rb < RB2; ++rb) ad[slot][rb] = bload2<0>(rd, st.vofs(lrow[rb], j), so);
                 };
                 auto issue_b = [&](int slot, int j) {
                     const uint32_t so = st.sofs(j);
@@ -474,9 +698,9 @@ __global__ __launch_bounds__(kThreads) void k_expert(Args a) {
                 }
 #pragma unroll
                 for (int i = 0; i < P; ++i) issue_b(i, i);
-                f32x4 acc[RB][NT];
+                f32x4 acc[RB2][NT];
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
+                for (int rb = 0; rb < RB2; ++rb)
 #pragma unroll
                     for (int tt = 0; tt < NT; ++tt) acc[rb][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
                 for (int s = 0; s < ns; s += P) {
@@ -485,7 +709,7 @@ __global__ __launch_bounds__(kThreads) void k_expert(Args a) {
 #pragma unroll
                         for (int i = hh * H; i < hh * H + H; ++i)
 #pragma unroll
-                            for (int rb = 0; rb < RB; ++rb)
+                            for (int rb = 0; rb < RB2; ++rb)
 #pragma unroll
                                 for (int tt = 0; tt < NT; ++tt) {
                                     acc[rb][tt] = F::mma(ad[i][rb], bh[i][tt], acc[rb][tt]);
@@ -501,17 +725,17 @@ __global__ __launch_bounds__(kThreads) void k_expert(Args a) {
                     }
                 }
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
+                for (int rb = 0; rb < RB2; ++rb)
 #pragma unroll
                     for (int tt = 0; tt < NT; ++tt) sm.red[wave][0][rb * NT + tt][lane] = acc[rb][tt];
                 __syncthreads();
-                if (wave < RB * NT) {
+                if (wave < RB2 * NT) {
                     const int rb = wave / NT, tt = wave - rb * NT;
                     f32x4 v = sm.red[0][0][wave][lane];
 #pragma unroll
                     for (int w = 1; w < kWaves; ++w) v += sm.red[w][0][wave][lane];
                     const int gi = base + tt * 16 + lr;
-                    const int i0 = t * RT + rb * kTile + 4 * q;
+                    const int i0 = t * RT2 + rb * kTile + 4 * q;
                     if (gi < g && i0 < a.d)  // d % 8 == 0: rows i0..i0+3 all valid
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro,
                                                                ((uint32_t)sm.grp[gi] * a.d + i0) * 4, 0, kSc1);
@@ -534,19 +758,34 @@ __global__ __launch_bounds__(kThreads) void k_expert(Args a) {
         }
         __syncthreads();  // O loads (sc1) below are issued after the last arrival was seen
         if (s_last) {
-            const int i0 = t * RT;
-            const int rows = min(RT, a.d - i0);
-            for (int o = tid; o < a.n * rows; o += kThreads) {
-                const int tok = o / rows, i = i0 + (o - tok * rows);
-                float acc = 0.f;
-                for (int j = 0; j < a.m; ++j) {
-                    const int s = tok * a.m + j;
-                    const int id = a.ids[s];
-                    if (id >= 0 && id < a.N)
-                        acc = fmaf(a.w[s], __hip_atomic_load(a.O + (size_t)s * a.d + i, __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_AGENT), acc);
+            // y_t = sum_j w_tj O_tj for 4 rows per thread, slots in increasing j;
+            // the O loads (sc1) of up to kCJ slots are in flight together
+            constexpr int kCJ = 8;
+            const int i0 = t * RT2;
+            const int q4 = min(RT2, a.d - i0) / 4;  // d % 8 == 0
+            const auto rO = rsrc(a.O, (uint32_t)nm * a.d * 4);
+            for (int o = tid; o < a.n * q4; o += kThreads) {
+                const int tok = o / q4, i = i0 + 4 * (o - tok * q4);
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int j0 = 0; j0 < a.m; j0 += kCJ) {
+                    u32x4 ov[kCJ];
+                    float wv[kCJ];
+                    bool ok[kCJ];
+#pragma unroll
+                    for (int jj = 0; jj < kCJ; ++jj) {
+                        const int s = tok * a.m + j0 + jj;
+                        const int id = j0 + jj < a.m ? a.ids[s] : -1;
+                        ok[jj] = id >= 0 && id < a.N;
+                        wv[jj] = ok[jj] ? a.w[s] : 0.f;
+                        ov[jj] = bload_sc1(rO, ok[jj] ? ((uint32_t)s * a.d + i) * 4 : kOOB);
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < kCJ; ++jj)
+                        if (ok[jj])
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) acc[r] = fmaf(wv[jj], __uint_as_float(ov[jj][r]), acc[r]);
                 }
-                float* yp = a.y + (size_t)tok * a.d + i;
+                f32x4* yp = reinterpret_cast<f32x4*>(a.y + (size_t)tok * a.d + i);
                 *yp = a.accumulate ? *yp + acc : acc;
             }
         }
@@ -665,8 +904,15 @@ int check_desc(const moe_layer_desc* d, int32_t n) {
 
 struct Plan {
     int units, T1, T2, nt, rb;
+    int g1, S1;  // gate/up work groups, K steps per gate/up tile
+    size_t part_off;
+    bool dpf;    // down items in register mode
+    int gl;      // register mode: tokens of h staged in LDS at a time
+    size_t lds;  // register mode: dynamic LDS bytes
     size_t h_off, o_off, sync_off, total;
 };
+
+constexpr int kHsBudget = 24 * 1024;  // LDS bytes for staged h (down items in register mode)
 
 Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     Plan p;
@@ -675,21 +921,50 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     p.nt = kind == MOE_KIND_SLOT ? 1 : (n <= 16 ? 1 : (n <= 32 ? 2 : 4));
     p.rb = p.nt == 4 ? 1 : 2;  // rows per item = 16 * rb; row blocks x token tiles <= 4
     p.T1 = (d->d_ff + kTile * p.rb - 1) / (kTile * p.rb);
-    p.T2 = (d->d_model + kTile * p.rb - 1) / (kTile * p.rb);
+    // register mode when a wave's share of the down contraction fits kPF steps
+    const bool bf = d->dtype == MOE_BF16;
+    const int es = bf ? 2 : 4, step = 64 / es;
+    const int s2 = (d->d_ff + step - 1) / step;
+    const int per_tok = (d->d_ff * es + 16) * (bf ? 2 : 1);  // staged bytes per token
+    const int gmax = kind == MOE_KIND_SLOT ? 1 : n;  // group size is at most n (valid ids)
+    // (and only when one LDS chunk of at most 16 tokens, one MFMA column tile,
+    // holds a whole group: several chunks would serialise their h loads and O
+    // stores)
+    p.dpf = (s2 + kWaves - 1) / kWaves <= kPF && gmax <= 16 && (int64_t)per_tok * gmax <= kHsBudget;
+    p.gl = p.dpf ? gmax : 0;
+    p.lds = p.dpf ? (size_t)p.gl * per_tok : 0;
+    const int rb2 = p.dpf ? 1 : p.rb;
+    p.T2 = (d->d_model + kTile * rb2 - 1) / (kTile * rb2);
+    // Gate/up work is cut into kCUs equal shares when there are between half and
+    // twice as many tiles as compute units: then no compute unit holds two tiles
+    // while another holds one.  Each share is at least half a tile, so a tile is
+    // shared by at most kMaxContrib work groups.  Otherwise one work group per
+    // tile (with more tiles, cutting them measured slower than the imbalance).
+    p.S1 = (d->d_model + step - 1) / step;
+    const int64_t tiles = (int64_t)p.units * p.T1;
+    const int64_t part_bytes = (int64_t)kMaxContrib * nm * d->d_ff * 8;
+    const bool split = tiles * 2 >= kCUs && tiles < 2 * kCUs && part_bytes <= (64ll << 20);
+    p.g1 = split ? kCUs : (int)tiles;
     p.sync_off = 0;
     p.h_off = (size_t)kSyncWords * 4;
     p.o_off = p.h_off + align_up((size_t)nm * d->d_ff * 4);
-    p.total = p.o_off + align_up((size_t)nm * d->d_model * 4);
+    p.part_off = p.o_off + align_up((size_t)nm * d->d_model * 4);
+    p.total = p.part_off + (split ? align_up((size_t)part_bytes) : 0);
     return p;
 }
 
 template <bool BF16, int MODE, int NT, int RB>
-void launch(const Args& args, int grid, hipStream_t st) {
+void launch(const Args& args, const Plan& p, int grid, hipStream_t st) {
     constexpr int step = Fmt<BF16>::kStep;
-    if (args.d % step == 0 && args.d_ff % step == 0)
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true>), dim3(grid), dim3(kThreads), 0, st, args);
+    const bool kf = args.d % step == 0 && args.d_ff % step == 0;
+    if (kf && p.dpf)
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, true>), dim3(grid), dim3(kThreads), p.lds, st, args);
+    else if (kf)
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, false>), dim3(grid), dim3(kThreads), 0, st, args);
+    else if (p.dpf)
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, true>), dim3(grid), dim3(kThreads), p.lds, st, args);
     else
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false>), dim3(grid), dim3(kThreads), 0, st, args);
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, false>), dim3(grid), dim3(kThreads), 0, st, args);
 }
 
 template <int MODE>
@@ -733,18 +1008,22 @@ int run_expert(const moe_layer_desc* d, const moe_layer_weights* W, const void* 
     args.T1 = p.T1;
     args.T2 = p.T2;
     args.accumulate = (d->flags & MOE_FLAG_ACCUMULATE) ? 1 : 0;
-    const int grid = p.units * (p.T1 + p.T2);
+    args.gl = p.gl;
+    args.g1 = p.g1;
+    args.S1 = p.S1;
+    args.part = reinterpret_cast<float*>(wsb + p.part_off);
+    const int grid = p.g1 + p.units * p.T2;
     (void)hipGetLastError();
     if (events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(events[0]), st);
     const bool bf = d->dtype == MOE_BF16;
     if (bf) {
-        if (p.nt == 1) launch<true, MODE, 1, 2>(args, grid, st);
-        else if (p.nt == 2) launch<true, MODE, 2, 2>(args, grid, st);
-        else launch<true, MODE, 4, 1>(args, grid, st);
+        if (p.nt == 1) launch<true, MODE, 1, 2>(args, p, grid, st);
+        else if (p.nt == 2) launch<true, MODE, 2, 2>(args, p, grid, st);
+        else launch<true, MODE, 4, 1>(args, p, grid, st);
     } else {
-        if (p.nt == 1) launch<false, MODE, 1, 2>(args, grid, st);
-        else if (p.nt == 2) launch<false, MODE, 2, 2>(args, grid, st);
-        else launch<false, MODE, 4, 1>(args, grid, st);
+        if (p.nt == 1) launch<false, MODE, 1, 2>(args, p, grid, st);
+        else if (p.nt == 2) launch<false, MODE, 2, 2>(args, p, grid, st);
+        else launch<false, MODE, 4, 1>(args, p, grid, st);
     }
     if (events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(events[1]), st);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
@@ -768,7 +1047,12 @@ int moe_route_group(const int32_t* ids, int32_t n, int32_t m, int32_t N, int32_t
 size_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t n, int32_t kind) {
     if (kind != MOE_KIND_SLOT && kind != MOE_KIND_DEDUP) return 0;
     if (check_desc(desc, n) != MOE_OK) return 0;
-    return plan_for(desc, n, kind).total;
+    size_t total = 0;  // largest over 1..n tokens (the split partial sums are not monotone in n)
+    for (int32_t k = 1; k <= n; ++k) {
+        const size_t t = plan_for(desc, k, kind).total;
+        total = t > total ? t : total;
+    }
+    return total;
 }
 
 int moe_kernels_per_call(int32_t kind) {

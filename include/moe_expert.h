@@ -102,11 +102,14 @@ int moe_route_group(const int32_t* ids, int32_t n, int32_t m, int32_t N, int32_t
                     int32_t* u_and_err, void* hip_stream);
 
 /* Workspace bytes that moe_expert_perslot (kind MOE_KIND_SLOT) or
- * moe_expert_dedup (MOE_KIND_DEDUP) needs for a pass of n tokens; 0 on invalid
- * arguments.  The workspace holds 160 KB of synchronisation counters (one per
- * 128-byte line), the per-slot hidden activations and the per-slot expert outputs:
- * 163840 + n*m*(d_ff + d_model)*4 bytes plus alignment.  A workspace sized for n
- * serves every smaller n of the same layer.  d_model is limited to 16384. */
+ * moe_expert_dedup (MOE_KIND_DEDUP) needs for passes of up to n tokens; 0 on
+ * invalid arguments.  For a pass of k tokens the workspace holds 224 KB of
+ * synchronisation counters (one per 128-byte line), the per-slot hidden
+ * activations and expert outputs (k*m*(d_ff + d_model)*4 bytes) and, when the
+ * pass's gate/up work is 128 to 511 row tiles, the partial sums of tiles that
+ * work groups share (3*k*m*d_ff*8 bytes), each piece aligned to 256 bytes.  The
+ * size returned is the largest over k = 1..n, so a workspace sized for n serves
+ * every smaller n of the same layer.  d_model is limited to 16384. */
 size_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t n, int32_t kind);
 
 /*

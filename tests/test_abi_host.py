@@ -72,8 +72,25 @@ def test_host_validation_rejects_before_launch():
     assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(Wm), fake, fake, fake, 4, fake, None, fake, 1 << 30,
                                 None) == _abi.MOE_E_INVAL
     need = L.moe_workspace_bytes(ctypes.byref(d), 4, 0)
-    assert need == 163840 + 4 * 2 * 128 * 4 + 4 * 2 * 64 * 4  # sync area + h + O (256-aligned pieces)
+    assert need == 229376 + 4 * 2 * 128 * 4 + 4 * 2 * 64 * 4  # sync area + h + O (256-aligned pieces)
     assert L.moe_workspace_bytes(ctypes.byref(d), 4, 1) == need
+    # 128 .. 511 gate/up tiles: the workspace also holds partial sums of split
+    # tiles, 3 contributors x n*m x d_ff x (gate, up) fp32 (per-slot: 44 tiles per
+    # slot, split for one token); the size is the largest over 1..n tokens
+    big = _desc(N=64, m=6, d_model=2048, d_ff=1408, dtype=_abi.MOE_BF16)
+
+    def one(n, split):
+        nm = n * 6
+        return 229376 + nm * 1408 * 4 + nm * 2048 * 4 + (3 * nm * 1408 * 8 if split else 0)
+
+    assert L.moe_workspace_bytes(ctypes.byref(big), 1, 0) == one(1, True)
+    assert L.moe_workspace_bytes(ctypes.byref(big), 1, 1) == one(1, True)
+    assert L.moe_workspace_bytes(ctypes.byref(big), 3, 0) == max(one(1, True), one(3, False))
+    assert L.moe_workspace_bytes(ctypes.byref(big), 8, 0) == one(8, False)
+    for k in (0, 1):  # n*m <= 256: n <= 42
+        sizes = [L.moe_workspace_bytes(ctypes.byref(big), n, k) for n in range(1, 43)]
+        assert all(sizes) and all(a <= b for a, b in zip(sizes, sizes[1:]))
+    assert L.moe_workspace_bytes(ctypes.byref(big), 43, 0) == 0
     assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 4, fake, None, fake, need - 1,
                                 None) == _abi.MOE_E_WORKSPACE
     assert L.moe_expert_dedup(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 4, fake, None, vp(0x1010), need,

@@ -2,8 +2,9 @@
 
 Bar: grouping bit-exact; y within rel-L2 5e-3 and max-abs 3e-2 of the fp32
 oracle on the same bf16-rounded inputs (fp32 layers: same bar); per-slot and
-deduplicating results bitwise equal (they add each token's slot outputs in the
-same order from identical per-slot products).
+deduplicating results agree to fp32 summation order (rel-L2 <= 1e-4: the two
+kernels may cut a gate/up tile's K range at different points), and every kernel
+is deterministic (bitwise equal results on repeated passes).
 """
 import itertools
 
@@ -17,7 +18,7 @@ import synth
 from synth import routing
 from synth.device import to_torch
 
-from .gpu_cases import DeviceLayer, assert_close, say
+from .gpu_cases import SUMMATION_TOL, DeviceLayer, assert_close, errors, say
 
 pytestmark = pytest.mark.gpu
 
@@ -57,15 +58,19 @@ def test_route_group_configs_and_invalid():
     _check_group(np.full((4, 2), 3, np.int32), 5)
 
 
-def _compare(dl, x, ids, w, what, shared=False, tokens=None, bitwise=True):
+def _agree(ys, yd, what):
+    rel, _ = errors(ys, yd)
+    assert rel <= SUMMATION_TOL, "%s: per-slot and dedup differ, rel_l2=%.3e" % (what, rel)
+
+
+def _compare(dl, x, ids, w, what, shared=False, tokens=None):
     ys, yd, info = dl.run(x, ids, w, shared=shared)
     assert info[0] == oracle.union_count(ids, dl.spec.N) and info[1] == 0
     ref = dl.oracle_y(x, ids, w, shared=shared, tokens=tokens)
     sel = slice(None) if tokens is None else tokens
     r1 = assert_close(ys[sel], ref, what + " perslot")
     r2 = assert_close(yd[sel], ref, what + " dedup")
-    if bitwise:
-        assert np.array_equal(ys, yd), what + ": per-slot and dedup differ bitwise"
+    _agree(ys, yd, what)
     return r1, r2
 
 
@@ -83,7 +88,11 @@ def test_tiny_fp32_many_seeds():
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("N,m,d,d_ff,n", [
     (5, 3, 72, 136, 1), (5, 3, 72, 136, 3), (5, 3, 72, 136, 17), (6, 2, 40, 24, 33),
-    (4, 4, 8, 8, 64), (12, 4, 264, 200, 64), (9, 1, 1032, 40, 20)])
+    (4, 4, 8, 8, 64), (12, 4, 264, 200, 64), (9, 1, 1032, 40, 20),
+    # d_ff too long for the down weights to sit in registers: the streaming down path
+    (7, 2, 136, 1560, 5), (7, 2, 136, 1560, 40),
+    # 128..1024 gate/up tiles: K ranges shared between work groups (split tiles)
+    (40, 4, 72, 1000, 3), (40, 4, 200, 520, 5)])
 def test_ragged_shapes(dtype, N, m, d, d_ff, n):
     say("ragged", dtype, N, m, d, d_ff, n)
     spec = synth.layer_spec("tiny", N=N, m=m, d=d, d_ff=d_ff, dtype=dtype, sigma=0.05)
@@ -126,7 +135,7 @@ def test_invalid_ids_skip_slot_and_flag():
     ref = dl.oracle_y(x, ids_ok, w_ok)
     assert_close(ys, ref, "invalid perslot")
     assert_close(yd, ref, "invalid dedup")
-    assert np.array_equal(ys, yd)
+    _agree(ys, yd, "invalid")
 
 
 def test_accumulate_and_determinism():
@@ -201,8 +210,9 @@ def test_mixtral_sampled_tokens():
 
 @pytest.mark.parametrize("kind", ["uniform", "correlated"])
 def test_repeated_passes_bitwise_stable(dsv2, kind):
-    """Many back-to-back passes on one workspace: every result bitwise equal to the
-    first, per-slot equal to dedup.  Data handed between workgroups (h, O) that
+    """Many back-to-back passes on one workspace, per-slot and dedup alternating:
+    every result bitwise equal to the first of its kind, the two kinds equal to
+    summation order.  Data handed between workgroups (h, O, partial sums) that
     were not yet visible, or counters not reset between calls, would break it."""
     spec = dsv2.spec
     tr = routing.make_trace(spec, kind, 256, seed=31, p=0.5)
@@ -213,12 +223,14 @@ def test_repeated_passes_bitwise_stable(dsv2, kind):
         x = to_torch(synth.pass_x(spec, 31, 0, n, n))
         ids, w = _ids_dev(ids_h), torch.from_numpy(w_h).cuda()
         say("repeat", kind, "n", n)
-        ref = efa.expert_perslot(dsv2.dev, x, ids, w, ws=ws).clone()
+        refs = [efa.expert_perslot(dsv2.dev, x, ids, w, ws=ws).clone(),
+                efa.expert_dedup(dsv2.dev, x, ids, w, ws=ws).clone()]
         outs = []
         for it in range(40):
             fn = efa.expert_perslot if it % 2 == 0 else efa.expert_dedup
             outs.append(fn(dsv2.dev, x, ids, w, ws=ws, info=info).clone())
         torch.cuda.synchronize()
-        for o in outs:
-            assert torch.equal(o, ref)
+        for it, o in enumerate(outs):
+            assert torch.equal(o, refs[it % 2]), (n, it)
+        _agree(refs[0].cpu().numpy(), refs[1].cpu().numpy(), "repeat n=%d" % n)
         assert int(info[2].item()) == 0
