@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 METRIC = "expert-op achieved HBM GB/s & % peak vs pass size n=1..8; dedup r(n), crossover n"
 SCRUB_BYTES = 1 << 30
+COPY_BYTES = 1 << 28
 
 
 class HipEvents:
@@ -91,6 +92,126 @@ def cpu_baseline(spec, host_w, passes, budget_s):
                       "wall time, single-threaded C oracle (double accumulate)" % (done, dt)}
 
 
+PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc {counter} -d $R/gpurun_out/pmc_{tag} "
+           "-o run --output-format csv -- python3 $R/bench.py --pmc-pass   (R = repository root)")
+PROF_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof -o run --output-format csv -- "
+            "python3 bench.py > gpurun_out/prof_bench.json")
+
+
+def _counter_rows(path):
+    import csv
+    return list(csv.DictReader(open(path)))
+
+
+def traffic_from(fetch_csv, write_csv, config):
+    """HBM bytes per per-slot launch from two counter runs of `--pmc-pass`.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
+    counter reads for the run's device copy of COPY_BYTES (read and written once),
+    then averaged over the per-slot launches, like the achieved figure."""
+    out = {}
+    for name, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = _counter_rows(path)
+        copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        cal = max(copy)  # the 256 MiB device copy is the largest copy of the run
+        factor = COPY_BYTES / (cal * 1024.0)
+        ke = [float(r["Counter_Value"]) for r in rows if "k_expert" in r["Kernel_Name"]]
+        out[name] = dict(copy_kib=cal, factor=factor, kernel_kib=ke, bytes=[v * 1024.0 * factor for v in ke])
+    n = len(out["fetch"]["bytes"])
+    assert n == len(out["write"]["bytes"]) and n > 0
+    per_launch = (sum(out["fetch"]["bytes"]) + sum(out["write"]["bytes"])) / n
+    return out, per_launch
+
+
+def write_traffic_summary(fetch_csv, write_csv, config, pass_json):
+    info = [json.loads(l) for l in open(pass_json) if l.startswith('{"pmc_pass"')][-1]
+    out, per_launch = traffic_from(fetch_csv, write_csv, config)
+    alg = [p["bytes"] for p in info["pmc_pass"]]
+    n = len(alg)
+    assert n == len(out["fetch"]["bytes"])
+    rec = {"kernel": "k_expert per-slot", "config": config, "launches": n,
+           "bytes_per_launch": round(per_launch, 1), "algorithmic_bytes_per_launch": round(sum(alg) / n, 1),
+           "fetch_factor": round(out["fetch"]["factor"], 4), "write_factor": round(out["write"]["factor"], 4),
+           "source_hash": info["source_hash"]}
+    lines = ["# HBM traffic of the per-slot k_expert launches, %s-shaped layer, n = 1..8, uniform + correlated" % config,
+             "", "Commands (one GPU; FETCH_SIZE and WRITE_SIZE in separate runs), then on any host:", "", "```",
+             PMC_CMD.format(counter="FETCH_SIZE", tag="fetch"), PMC_CMD.format(counter="WRITE_SIZE", tag="write"),
+             "python3 bench.py --traffic-from gpurun_out/pmc_fetch/run_counter_collection.csv "
+             "gpurun_out/pmc_write/run_counter_collection.csv gpurun_out/pmc.log", "```", "",
+             "Calibration: the run's device copy of %d bytes reads %.1f KiB FETCH_SIZE and %.1f KiB WRITE_SIZE, so "
+             "the counters are scaled by %.4f and %.4f." % (COPY_BYTES, out["fetch"]["copy_kib"],
+                                                             out["write"]["copy_kib"], out["fetch"]["factor"],
+                                                             out["write"]["factor"]),
+             "", "| routing | n | algorithmic MB | fetched MB (scaled) | written MB (scaled) | fetched / algorithmic |",
+             "|---|---|---|---|---|---|"]
+    for i, p in enumerate(info["pmc_pass"]):
+        fb, wb = out["fetch"]["bytes"][i], out["write"]["bytes"][i]
+        lines.append("| %s | %d | %.1f | %.1f | %.2f | %.3f |" % (p["kind"], p["n"], p["bytes"] / 1e6, fb / 1e6,
+                                                                 wb / 1e6, fb / p["bytes"]))
+    lines += ["", "Per launch (average over the %d launches): %.1f MB counted, %.1f MB algorithmic." % (
+        n, per_launch / 1e6, sum(alg) / n / 1e6), "", "traffic-json: " + json.dumps(rec)]
+    path = os.path.join(ROOT, "profiles", "traffic_k_expert_perslot_%s.md" % config)
+    open(path, "w").write("\n".join(lines) + "\n")
+    print(path)
+
+
+def read_traffic(config):
+    """bytes per launch from the committed counter summary, if it is for this kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic_k_expert_perslot_%s.md" % config)
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic-json: "):
+            rec = json.loads(line[len("traffic-json: "):])
+            if rec.get("source_hash") == source_hash():
+                return rec["bytes_per_launch"]
+    return None
+
+
+def write_profile_summary(prof_dir, bench_json, config):
+    """Short markdown summary of a `rocprofv3 --kernel-trace --stats` run of this bench."""
+    import collections
+    import re
+    trace = [f for f in os.listdir(prof_dir) if f.endswith("kernel_trace.csv")][0]
+    stats = [f for f in os.listdir(prof_dir) if f.endswith("kernel_stats.csv")][0]
+    d = collections.defaultdict(list)
+    for r in _counter_rows(os.path.join(prof_dir, trace)):
+        m = re.search(r"(k_\w+)(<[^>]*>)?", r["Kernel_Name"])
+        if not m:
+            continue
+        key = (m.group(1) + (m.group(2) or ""), int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
+        d[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000)
+    b = [json.loads(l) for l in open(bench_json) if l.startswith('{"metric"')][-1]
+    lines = ["# k_expert (per-slot and deduplicating), %s-shaped layer, n = 1..8, uniform + correlated routing" % config,
+             "", "Command (from the repository root, one MI355X):", "", "```", PROF_CMD, "```", "",
+             "## rocprofv3 --stats (all kernels of the run)", "", "| kernel | calls | avg us | % of GPU time |",
+             "|---|---|---|---|"]
+    for r in _counter_rows(os.path.join(prof_dir, stats)):
+        m = re.search(r"(k_\w+<[^>]*>|k_\w+)", r["Name"])
+        short = m.group(1) if m else r["Name"].split("(")[0][:60]
+        lines.append("| `%s` | %s | %.2f | %.2f |" % (short, r["Calls"], float(r["AverageNs"]) / 1000,
+                                                      float(r["Percentage"])))
+    lines += ["", "## Per-launch durations of the expert kernels by grid size (kernel trace)", "",
+              "| kernel | workgroups | launches | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for k in sorted(d):
+        v = d[k]
+        lines.append("| `%s` | %d | %d | %.2f | %.2f | %.2f |" % (k[0], k[1], len(v), sum(v) / len(v), min(v), max(v)))
+    slot = [v for k, vs in d.items() if k[0].startswith("k_expert<true, 0") for v in vs]
+    rf = b["roofline"]
+    lines += ["", "## Bench line of the same run (HIP events on the launch stream)", "",
+              "- value: %.1f GB/s (all passes, both kernels)" % b["value"],
+              "- per-slot kernel: avg %.2f us per launch by events, %.2f us by the kernel trace (%d launches, "
+              "warm-up included); %.0f algorithmic bytes per launch; achieved %.1f GB/s = %.3f of 8 TB/s" % (
+                  rf["avg_launch_us"], sum(slot) / max(len(slot), 1), len(slot), rf["algorithmic_bytes_per_launch"],
+                  rf["achieved"], rf["frac"]),
+              "- deduplicating kernel: avg %.2f us, achieved %.1f GB/s" % (rf["dedup_kernel"]["avg_launch_us"],
+                                                                           rf["dedup_kernel"]["achieved"]),
+              "- source hash %s" % b.get("source_hash")]
+    path = os.path.join(ROOT, "profiles", "k_expert_%s_n1-8.md" % config)
+    open(path, "w").write("\n".join(lines) + "\n")
+    print(path)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,7 +223,20 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-scrub", action="store_true")
     ap.add_argument("--details", default="", help="write per-pass records (JSONL) here")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="for a counter run: one step of per-slot passes (both routings, n=1..nmax), each after "
+                         "the 1 GiB read flush, then a 256 MiB device copy; prints what ran")
+    ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "PASS_LOG"),
+                    help="write profiles/traffic_k_expert_perslot_<config>.md from two counter runs (no GPU)")
+    ap.add_argument("--profile-summary", nargs=2, metavar=("PROF_DIR", "BENCH_JSON"),
+                    help="write profiles/k_expert_<config>_n1-8.md from a kernel-trace run (no GPU)")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic_summary(args.traffic_from[0], args.traffic_from[1], args.config, args.traffic_from[2])
+        return
+    if args.profile_summary:
+        write_profile_summary(*args.profile_summary, args.config)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the expert operation here runs on a single MI355X and has no "
               "multi-GPU path; run with --gpus 1", file=sys.stderr)
@@ -179,6 +313,26 @@ def main():
                     recs.append(dict(kind=kind, n=n, step=s, U=p["U"], bytes_slot=n * spec.m * w_exp,
                                      bytes_dedup=p["U"] * w_exp, t_slot_ms=t_slot, t_dedup_ms=t_dedup))
 
+    if args.pmc_pass:
+        # Counter run: the flush (a plain read of SCRUB_BYTES) and a device copy
+        # (COPY_BYTES read and written) calibrate FETCH_SIZE and WRITE_SIZE; the
+        # per-slot launches in between are the ones the bench times.
+        order = []
+        for kind, _ in kinds:
+            for n in nvals:
+                p = passes[(kind, n, args.warmup)]
+                flush()
+                efa.expert_perslot(layer, p["x"], p["ids"], p["w"], y=ys[n], ws=ws, stream=stream)
+                order.append(dict(kind=kind, n=n, bytes=n * spec.m * w_exp))
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_pass": order, "flush_read_bytes": SCRUB_BYTES, "copy_bytes": COPY_BYTES,
+                          "source_hash": source_hash()}))
+        return
+
     for s in range(args.warmup):
         run_step(s, False)
     torch.cuda.synchronize()
@@ -224,12 +378,7 @@ def main():
     dd_bytes = sum(r["bytes_dedup"] for r in recs)
     dd_s = sum(r["t_dedup_ms"] for r in recs) / 1e3
     achieved = slot_bytes / slot_s / 1e9
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", "traffic_k_expert_perslot_%s.json" % args.config)
-    if os.path.exists(tpath):
-        tj = json.load(open(tpath))
-        if tj.get("source_hash") == source_hash():
-            traffic = tj.get("bytes_per_launch")
+    traffic = read_traffic(args.config)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
                 "kernel": "k_expert<bf16, per-slot> (whole operation, one launch)", "launches": n_launch,
