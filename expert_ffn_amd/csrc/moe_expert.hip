@@ -204,20 +204,23 @@ struct Smem {
     int32_t ids[MOE_MAX_SLOTS];
     int32_t grp[MOE_MAX_SLOTS];    // slots of this workgroup's unit, increasing
     uint32_t pres[MOE_MAX_EXPERTS / 32];
-    int32_t wsum[kWaves];
-    int32_t meta[4];               // e, g, U, flag
+    int32_t meta[4];               // [3]: id status flag
     int32_t fin;                   // this work group finalises a split gate/up tile
 };
 
 // Stable grouping of the pass's slots by expert, in LDS, for distinct expert
-// number `u` (ids in increasing order).  Also the number U of distinct in-range
-// experts and, when want_status, MOE_E_IDS for ids out of range or repeated within
-// a token.  Leaves e (or -1), g in sm.meta and the slots in sm.grp.
+// number `u` (ids in increasing order): returns e (or -1 when u >= U), g and U, and
+// with `group` writes the unit's slots, increasing, to sm.grp[0..g).  Every wave
+// computes the presence scan and the ranks itself (and writes all of sm.grp), so
+// no barrier is needed after it.  With want_status, sm.meta[3] is set for ids out
+// of range or repeated within a token (read after the call by thread 0).
 template <int NB>
-__device__ void group_prologue(const Args& a, Smem<NB>& sm, int u, bool want_status) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ void group_prologue(const Args& a, Smem<NB>& sm, int u, bool want_status, bool group, int& e_out,
+                               int& g_out, int& U_out) {
+    const int tid = threadIdx.x, lane = tid & 63;
     const int nm = a.n * a.m;
     const int nwords = (a.N + 31) >> 5;
+    __syncthreads();  // the previous unit's reads of sm are done
     if (tid < nwords) sm.pres[tid] = 0u;
     if (tid == 0) sm.meta[3] = 0;
     const int id = tid < nm ? a.ids[tid] : -1;
@@ -234,44 +237,40 @@ __device__ void group_prologue(const Args& a, Smem<NB>& sm, int u, bool want_sta
         if (bad) atomicOr(&sm.meta[3], 1);
     }
     __syncthreads();
-    if (wave == 0) {
-        // prefix popcount over the presence words (<= 32 words)
-        const uint32_t word = lane < nwords ? sm.pres[lane] : 0u;
-        int c = __popc(word);
-        int incl = c;
+    // prefix popcount over the presence words (<= 32 words, lanes 0..31)
+    const uint32_t word = lane < nwords ? sm.pres[lane] : 0u;
+    const int c = __popc(word);
+    int incl = c;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int v = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += v;
-        }
-        const int U = __shfl(incl, 63, 64);
-        const int excl = incl - c;
-        if (lane == 0) {
-            sm.meta[2] = U;
-            sm.meta[0] = -1;
-        }
-        if (u < U && u >= excl && u < incl) {
-            uint32_t wv = word;
-            for (int k = u - excl; k > 0; --k) wv &= wv - 1;  // drop the lower set bits
-            sm.meta[0] = lane * 32 + __ffs(wv) - 1;
+    for (int o = 1; o < 32; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+    }
+    const int U = __shfl(incl, 31, 64);
+    const int excl = incl - c;
+    const bool mine = lane < 32 && u >= excl && u < incl;
+    int cand = -1;
+    if (mine) {
+        uint32_t wv = word;
+        for (int k = u - excl; k > 0; --k) wv &= wv - 1;  // drop the lower set bits
+        cand = lane * 32 + __ffs(wv) - 1;
+    }
+    const unsigned long long mb = __ballot(mine);
+    const int e = mb ? __shfl(cand, __ffsll((long long)mb) - 1, 64) : -1;
+    int g = 0;
+    if (group && e >= 0) {
+#pragma unroll
+        for (int i = 0; i < MOE_MAX_SLOTS / 64; ++i) {
+            const int s = lane + 64 * i;
+            const bool f = s < nm && sm.ids[s] == e;
+            const unsigned long long bal = __ballot(f);
+            if (f) sm.grp[g + __popcll(bal & ((1ull << lane) - 1ull))] = s;
+            g += __popcll(bal);
         }
     }
-    __syncthreads();
-    const int e = sm.meta[0];
-    if (e >= 0) {
-        const bool f = tid < nm && sm.ids[tid] == e;
-        const unsigned long long bal = __ballot(f);
-        const int rank = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0) sm.wsum[wave] = __popcll(bal);
-        __syncthreads();
-        int off = 0;
-        for (int w = 0; w < wave; ++w) off += sm.wsum[w];
-        if (f) sm.grp[off + rank] = tid;
-        if (tid == 0) sm.meta[1] = sm.wsum[0] + sm.wsum[1] + sm.wsum[2] + sm.wsum[3];
-    } else if (tid == 0) {
-        sm.meta[1] = 0;
-    }
-    __syncthreads();
+    e_out = e;
+    g_out = g;
+    U_out = U;
 }
 
 // Bounded wait until *p >= target (one thread).  Returns false on expiry.
@@ -504,16 +503,17 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
     // the ids' status (work group 0).
     auto resolve = [&](int u, bool status, int& e, int& g) {
         if (MODE == kDedup || status) {
-            group_prologue<NT * RB>(a, sm, MODE == kDedup ? u : 0, status);
+            int U;
+            group_prologue<NT * RB>(a, sm, MODE == kDedup ? u : 0, status, MODE == kDedup, e, g, U);
             if (status && tid == 0) {
-                a.info[0] = sm.meta[2];
+                a.info[0] = U;
                 a.info[1] = sm.meta[3] ? MOE_E_IDS : MOE_OK;
                 a.info[2] = MOE_OK;  // a bounded wait that expires later overwrites this
             }
         }
         if (MODE == kDedup) {
-            e = uni(sm.meta[0]);
-            g = uni(sm.meta[1]);
+            e = uni(e);
+            g = uni(g);
         } else {
             const int id = uni(a.ids[u]);
             e = (id >= 0 && id < a.N) ? id : -1;

@@ -127,8 +127,9 @@ size_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t n, int32_t kind);
  *        and the workspace must be zero-filled again
  *   ws   device workspace, ws_bytes >= moe_workspace_bytes(desc, n, MOE_KIND_SLOT),
  *        256-byte aligned, zero-filled before first use (see above).
- * Per token, slot contributions are added in increasing j, so the result is
- * deterministic and equal, bit for bit, to moe_expert_dedup's.
+ * Per token, slot contributions are added in increasing j.  The result is
+ * deterministic (bitwise equal over repeated calls) and equal to
+ * moe_expert_dedup's up to fp32 summation order.
  */
 int moe_expert_perslot(const moe_layer_desc* desc, const moe_layer_weights* weights,
                        const void* x, const int32_t* ids, const float* w, int32_t n, float* y,
