@@ -212,6 +212,186 @@ def write_profile_summary(prof_dir, bench_json, config):
     print(path)
 
 
+A_GRID = [i / 21.0 for i in range(22)]  # acceptance values of the best-draft-length staircase
+
+
+def step_model_section(efa, spec, rows, shared_us, layers=1):
+    """The step-time model fed by the measured times of one routing: E_p(n) is the
+    mean requested bytes of a pass, beta_p(n) = E_p(n) / measured kernel time (fixed
+    work folded in, phi = 0), D = the shared experts' bytes read once per pass with
+    beta_D = D / their measured time, t0 = h = 0; k*(a) over 22 acceptance values."""
+    nmax = len(rows)
+    E = [[r["bytes_slot"] for r in rows], [r["bytes_dedup"] for r in rows]]
+    beta = [[r["bytes_slot"] / (r["us_slot"] * 1e-6) for r in rows],
+            [r["bytes_dedup"] / (r["us_dedup"] * 1e-6) for r in rows]]
+    D = float(spec.n_shared * spec.expert_bytes)
+    beta_D = D / (sum(shared_us) / len(shared_us) * 1e-6) if D > 0 and shared_us else 1.0
+    mW = layers * spec.m * spec.expert_bytes  # expert bytes of one token over the layers of a pass
+    out = efa.step_time_model(nmax, A_GRID, mW, E, beta, D=D, beta_D=beta_D)
+    return {"inputs": {"m_W": mW, "D": D, "beta_D_GBps": round(beta_D / 1e9, 1),
+                       "t0": 0.0, "h": 0.0, "phi": "folded into the measured times"},
+            "a": [round(a, 4) for a in A_GRID],
+            "kstar_slot": out["kstar"][0].tolist(), "kstar_dedup": out["kstar"][1].tolist(),
+            "speedup_slot": [round(v, 4) for v in out["speedup"][0].tolist()],
+            "speedup_dedup": [round(v, 4) for v in out["speedup"][1].tolist()],
+            "a0": [round(v, 5) for v in out["a0"].tolist()],
+            "step_points_slot": [round(v, 5) for v in out["step_point"][0][1:].tolist()],
+            "step_points_dedup": [round(v, 5) for v in out["step_point"][1][1:].tolist()],
+            "tau_us_slot": [round(v * 1e6, 2) for v in out["tau"][0].tolist()],
+            "tau_us_dedup": [round(v * 1e6, 2) for v in out["tau"][1].tolist()],
+            "crossover_model": out["crossover"]}
+
+
+def per_n_rows(recs, nvals):
+    rows = []
+    for n in nvals:
+        R = [r for r in recs if r["n"] == n]
+        bs, bd = sum(r["bytes_slot"] for r in R), sum(r["bytes_dedup"] for r in R)
+        ts, td = sum(r["t_slot_ms"] for r in R) / 1e3, sum(r["t_dedup_ms"] for r in R) / 1e3
+        gs, gd = bs / ts / 1e9, bd / td / 1e9
+        rows.append(dict(n=n, gbps_slot=round(gs, 1), gbps_dedup=round(gd, 1),
+                         frac_slot=round(gs / PEAK_HBM_GBPS, 4), frac_dedup=round(gd / PEAK_HBM_GBPS, 4),
+                         r=round(gd / gs, 4), u=round(bd / bs, 4),
+                         us_slot=round(ts / len(R) * 1e6, 2), us_dedup=round(td / len(R) * 1e6, 2),
+                         bytes_slot=bs / len(R), bytes_dedup=bd / len(R),
+                         mean_U=round(sum(r["U"] for r in R) / len(R), 2)))
+    return rows
+
+
+def crossover_of(rows):
+    """Smallest n >= 2 from which the deduplicating kernel stays faster (0: none)."""
+    cross = 0
+    for r in reversed(rows):
+        if r["n"] < 2 or r["us_slot"] - r["us_dedup"] <= 0:
+            break
+        cross = r["n"]
+    return cross
+
+
+def strip_bytes(rows):
+    return [{k: v for k, v in r.items() if not k.startswith("bytes_")} for r in rows]
+
+
+def extra_configs(args, torch, efa, synth, routing, ev, flush, stream):
+    """The other workloads: the Qwen3-30B-A3B-shaped layer 48 times back to back per
+    pass (zipf routing), the 32-node draft tree on that layer, and the
+    Mixtral-8x7B-shaped layer (uniform and repeat-0.6 routing).  Weights from the
+    seeded device generator.  Each pass timed alone after the read flush."""
+    from synth.device import device_layer_weights
+    out = {}
+    e2 = ev.make(2)
+    sh = stream.cuda_stream
+
+    def xdev(spec, n, key):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(key)
+        return torch.randn(n, spec.d, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+    def timed(fn):
+        flush()
+        ev.record(e2[0], sh)
+        fn()
+        ev.record(e2[1], sh)
+        return ev.ms(e2[0], e2[1])
+
+    # ---- Qwen3-shaped: 48 layers back to back ----
+    spec = synth.CONFIGS["qwen3"]
+    L = spec.layers
+    layers = [efa.Layer(*device_layer_weights(spec, args.seed, l), m=spec.m) for l in range(L)]
+    T = 1024
+    traces = [routing.make_trace(spec, "zipf", T, seed=args.seed, layer=l, s=1.1) for l in range(L)]
+    ws = layers[0].workspace(8)
+    w_exp = spec.expert_bytes
+    reps = 3
+    qrows = []
+    recs = []
+    lib = efa.lib()
+    vp = ctypes.c_void_p
+    descs = [l.desc() for l in layers]
+
+    def argsets(n, x, dev, y):  # prebuilt C-ABI arguments, so 48 launches queue faster than they run
+        return [(ctypes.byref(descs[l]), ctypes.byref(layers[l]._weights), vp(x.data_ptr()), vp(dev[l][0].data_ptr()),
+                 vp(dev[l][1].data_ptr()), n, vp(y.data_ptr()), None, vp(ws.data_ptr()), ws.numel(), vp(sh))
+                for l in range(L)]
+
+    def run_all(fn, sets):
+        for a in sets:
+            assert fn(*a) == 0
+    for n in range(1, 9):
+        starts = routing.window_starts(T, n, reps + 1, seed=args.seed)
+        y = torch.empty(n, spec.d, dtype=torch.float32, device="cuda")
+        x = xdev(spec, n, 1000 + n)
+        for rp in range(reps + 1):
+            win = [routing.window(traces[l], int(starts[rp]), n) for l in range(L)]
+            dev = [(torch.from_numpy(i).cuda(), torch.from_numpy(w).cuda()) for i, w in win]
+            U = [len(set(i.reshape(-1).tolist())) for i, _ in win]
+            sets = argsets(n, x, dev, y)
+            ts = timed(lambda: run_all(lib.moe_expert_perslot, sets))
+            td = timed(lambda: run_all(lib.moe_expert_dedup, sets))
+            if rp > 0:
+                recs.append(dict(n=n, U=sum(U) / L, bytes_slot=L * n * spec.m * w_exp, bytes_dedup=sum(U) * w_exp,
+                                 t_slot_ms=ts, t_dedup_ms=td))
+    qrows = per_n_rows(recs, range(1, 9))
+    out["qwen3_x48"] = {"workload": "qwen3-shaped layer x48 back to back per pass (N=128, m=8, d=2048, d_ff=768, "
+                                    "bf16), zipf(s=1.1) routing per layer, %d passes per n" % reps,
+                        "per_n": strip_bytes(qrows), "crossover": crossover_of(qrows),
+                        "step_model": step_model_section(efa, spec, qrows, [], layers=L)}
+
+    # ---- 32-node draft tree on one Qwen3-shaped layer ----
+    tl = layers[0]
+    trecs = []
+    ntrees = 32
+    y = torch.empty(32, spec.d, dtype=torch.float32, device="cuda")
+    ws32 = tl.workspace(32)
+    x = xdev(spec, 32, 77)
+    for i in range(ntrees + 1):
+        _, ttr = routing.tree_routing(spec.N, spec.m, 0.5, routing.rng_for(args.seed, 0, "tree", i))
+        ids, w = torch.from_numpy(ttr.ids).cuda(), torch.from_numpy(ttr.w).cuda()
+        U = len(set(ttr.ids.reshape(-1).tolist()))
+        ts = timed(lambda: efa.expert_perslot(tl, x, ids, w, y=y, ws=ws32, stream=stream))
+        td = timed(lambda: efa.expert_dedup(tl, x, ids, w, y=y, ws=ws32, stream=stream))
+        if i > 0:
+            trecs.append(dict(n=32, U=U, bytes_slot=32 * spec.m * w_exp, bytes_dedup=U * w_exp, t_slot_ms=ts,
+                              t_dedup_ms=td))
+    trow = per_n_rows(trecs, [32])[0]
+    out["tree"] = {"workload": "32-node ancestor-closed draft tree (1+1+2+4+8+16, children reuse parent experts "
+                               "with p=0.5) on one qwen3-shaped layer, %d seeded trees" % ntrees,
+                   **{k: v for k, v in trow.items() if not k.startswith("bytes_")},
+                   "bytes_slot": trow["bytes_slot"], "bytes_dedup_mean": trow["bytes_dedup"]}
+    del layers, tl
+    torch.cuda.empty_cache()
+
+    # ---- Mixtral-shaped ----
+    spec = synth.CONFIGS["mixtral"]
+    ml = efa.Layer(*device_layer_weights(spec, args.seed, 0), m=spec.m)
+    wsm = ml.workspace(8)
+    w_exp = spec.expert_bytes
+    mix = {}
+    for kind, kw in (("uniform", {}), ("correlated", {"p": 0.6})):
+        tr = routing.make_trace(spec, kind, T, seed=args.seed, **kw)
+        mrecs = []
+        for n in range(1, 9):
+            starts = routing.window_starts(T, n, reps + 1, seed=args.seed + 5)
+            y = torch.empty(n, spec.d, dtype=torch.float32, device="cuda")
+            x = xdev(spec, n, 2000 + n)
+            for rp in range(reps + 1):
+                i_h, w_h = routing.window(tr, int(starts[rp]), n)
+                ids, w = torch.from_numpy(i_h).cuda(), torch.from_numpy(w_h).cuda()
+                ts = timed(lambda: efa.expert_perslot(ml, x, ids, w, y=y, ws=wsm, stream=stream))
+                td = timed(lambda: efa.expert_dedup(ml, x, ids, w, y=y, ws=wsm, stream=stream))
+                if rp > 0:
+                    U = len(set(i_h.reshape(-1).tolist()))
+                    mrecs.append(dict(n=n, U=U, bytes_slot=n * spec.m * w_exp, bytes_dedup=U * w_exp, t_slot_ms=ts,
+                                      t_dedup_ms=td))
+        rows = per_n_rows(mrecs, range(1, 9))
+        mix[kind] = {"per_n": strip_bytes(rows), "crossover": crossover_of(rows)}
+    out["mixtral"] = {"workload": "mixtral-shaped layer (N=8, m=2, d=4096, d_ff=14336, bf16), %d passes per n" % reps,
+                      **mix}
+    del ml
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +403,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-scrub", action="store_true")
     ap.add_argument("--details", default="", help="write per-pass records (JSONL) here")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other workloads (qwen3 x48, draft tree, mixtral) after the headline one")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for a counter run: one step of per-slot passes (both routings, n=1..nmax), each after "
                          "the 1 GiB read flush, then a 256 MiB device copy; prints what ran")
@@ -342,29 +524,31 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
 
+    # the shared experts' pass (read once per pass whatever the routing): D(n) of the step model
+    shared_us = []
+    if spec.n_shared:
+        sh_host = synth.layer_weights(spec, args.seed, shared=True)
+        shl = efa.Layer(*(to_torch(a) for a in sh_host), m=spec.n_shared)
+        sws = shl.workspace(nvals[-1])
+        e2 = ev.make(2)
+        for n in nvals:
+            sids = torch.arange(spec.n_shared, dtype=torch.int32, device="cuda").repeat(n, 1).contiguous()
+            sw = torch.ones(n, spec.n_shared, dtype=torch.float32, device="cuda")
+            x = passes[(kinds[0][0], n, 0)]["x"]
+            tl = []
+            for rep in range(4):
+                flush()
+                efa.expert_dedup(shl, x, sids, sw, y=ys[n], ws=sws, stream=stream, events=e2)
+                tl.append(ev.ms(e2[0], e2[1]) * 1e3)
+            shared_us.append(sorted(tl[1:])[1])
+        del shl
+
     # aggregate (bytes and times summed over the timed passes)
     per_kind = {}
     for kind, _ in kinds:
-        rows = []
-        S = {}
-        for n in nvals:
-            R = [r for r in recs if r["kind"] == kind and r["n"] == n]
-            bs, bd = sum(r["bytes_slot"] for r in R), sum(r["bytes_dedup"] for r in R)
-            ts, td = sum(r["t_slot_ms"] for r in R) / 1e3, sum(r["t_dedup_ms"] for r in R) / 1e3
-            gs, gd = bs / ts / 1e9, bd / td / 1e9
-            S[n] = (ts - td) / len(R)
-            rows.append(dict(n=n, gbps_slot=round(gs, 1), gbps_dedup=round(gd, 1),
-                             frac_slot=round(gs / PEAK_HBM_GBPS, 4), frac_dedup=round(gd / PEAK_HBM_GBPS, 4),
-                             r=round(gd / gs, 4), u=round(bd / bs, 4),
-                             us_slot=round(ts / len(R) * 1e6, 2), us_dedup=round(td / len(R) * 1e6, 2),
-                             mean_U=round(sum(r["U"] for r in R) / len(R), 2)))
-        cross = 0
-        for n in range(nvals[-1], 1, -1):
-            if S[n] > 0:
-                cross = n
-            else:
-                break
-        per_kind[kind] = dict(per_n=rows, crossover=cross)
+        rows = per_n_rows([r for r in recs if r["kind"] == kind], nvals)
+        per_kind[kind] = dict(per_n=strip_bytes(rows), crossover=crossover_of(rows),
+                              step_model=step_model_section(efa, spec, rows, shared_us))
 
     tot_bytes = sum(r["bytes_slot"] + r["bytes_dedup"] for r in recs)
     tot_s = sum(r["t_slot_ms"] + r["t_dedup_ms"] for r in recs) / 1e3
@@ -389,6 +573,16 @@ def main():
                                  "algorithmic_bytes_per_launch": round(dd_bytes / n_launch, 1)}}
 
     cpu = cpu_baseline(spec, host_w, host_passes, args.cpu_budget)
+    extras = {}
+    if spec.n_shared:
+        extras["shared_experts"] = {"workload": "%d always-on shared experts, weight 1, every token: one "
+                                                "deduplicating call per pass (the D(n) bytes of the step model)"
+                                                % spec.n_shared, "us_per_n": [round(v, 2) for v in shared_us],
+                                    "bytes": spec.n_shared * spec.expert_bytes}
+    if not args.no_extras and args.config == "dsv2lite":
+        del passes, layer
+        torch.cuda.empty_cache()
+        extras.update(extra_configs(args, torch, efa, synth, routing, ev, flush, stream))
 
     out = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
@@ -397,7 +591,7 @@ def main():
                args.config, nvals[-1], "+".join(k for k, _ in kinds)),
                "N": spec.N, "m": spec.m, "d_model": spec.d, "d_ff": spec.d_ff, "passes_per_step": len(kinds) * len(nvals) * 2,
                "scrub_bytes": 0 if args.no_scrub else SCRUB_BYTES},
-           "roofline": roofline, "cpu_baseline": cpu, "results": per_kind,
+           "roofline": roofline, "cpu_baseline": cpu, "results": per_kind, "extras": extras,
            "wall_s_timed": round(wall, 3), "setup_s": round(setup_s, 1), "source_hash": source_hash()}
     if args.details:
         with open(args.details, "w") as f:
