@@ -95,7 +95,7 @@ def cpu_baseline(spec, host_w, passes, budget_s):
 PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc {counter} -d $R/gpurun_out/pmc_{tag} "
            "-o run --output-format csv -- python3 $R/bench.py --pmc-pass   (R = repository root)")
 PROF_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof -o run --output-format csv -- "
-            "python3 bench.py > gpurun_out/prof_bench.json")
+            "python3 bench.py --no-extras > gpurun_out/prof_bench.json")
 
 
 def _counter_rows(path):
@@ -297,7 +297,7 @@ def extra_configs(args, torch, efa, synth, routing, ev, flush, stream):
     # ---- Qwen3-shaped: 48 layers back to back ----
     spec = synth.CONFIGS["qwen3"]
     L = spec.layers
-    layers = [efa.Layer(*device_layer_weights(spec, args.seed, l), m=spec.m) for l in range(L)]
+    layers = [efa.Layer(*device_layer_weights(spec, args.seed, l), m=spec.m).packed_copy() for l in range(L)]
     T = 1024
     traces = [routing.make_trace(spec, "zipf", T, seed=args.seed, layer=l, s=1.1) for l in range(L)]
     ws = layers[0].workspace(8)
@@ -363,7 +363,7 @@ def extra_configs(args, torch, efa, synth, routing, ev, flush, stream):
 
     # ---- Mixtral-shaped ----
     spec = synth.CONFIGS["mixtral"]
-    ml = efa.Layer(*device_layer_weights(spec, args.seed, 0), m=spec.m)
+    ml = efa.Layer(*device_layer_weights(spec, args.seed, 0), m=spec.m).packed_copy()
     wsm = ml.workspace(8)
     w_exp = spec.expert_bytes
     mix = {}
@@ -438,7 +438,8 @@ def main():
     T = 4096
     t_setup = time.perf_counter()
     host_w = synth.layer_weights(spec, args.seed)
-    layer = efa.Layer(*(to_torch(a) for a in host_w), m=spec.m)
+    # W_down in the packed layout (moe_pack_w_down), done once at weight-load time
+    layer = efa.Layer(*(to_torch(a) for a in host_w), m=spec.m).packed_copy()
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     nsteps_total = args.warmup + args.steps
@@ -528,7 +529,7 @@ def main():
     shared_us = []
     if spec.n_shared:
         sh_host = synth.layer_weights(spec, args.seed, shared=True)
-        shl = efa.Layer(*(to_torch(a) for a in sh_host), m=spec.n_shared)
+        shl = efa.Layer(*(to_torch(a) for a in sh_host), m=spec.n_shared).packed_copy()
         sws = shl.workspace(nvals[-1])
         e2 = ev.make(2)
         for n in nvals:
@@ -589,7 +590,8 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "%s-shaped MoE layer expert op, n=1..%d, routing %s" % (
                args.config, nvals[-1], "+".join(k for k, _ in kinds)),
-               "N": spec.N, "m": spec.m, "d_model": spec.d, "d_ff": spec.d_ff, "passes_per_step": len(kinds) * len(nvals) * 2,
+               "N": spec.N, "m": spec.m, "d_model": spec.d, "d_ff": spec.d_ff, "w_down_layout": "packed",
+               "passes_per_step": len(kinds) * len(nvals) * 2,
                "scrub_bytes": 0 if args.no_scrub else SCRUB_BYTES},
            "roofline": roofline, "cpu_baseline": cpu, "results": per_kind, "extras": extras,
            "wall_s_timed": round(wall, 3), "setup_s": round(setup_s, 1), "source_hash": source_hash()}

@@ -9,6 +9,6 @@ from ._abi import (  # noqa: F401
     MOE_KIND_DEDUP, MOE_KIND_SLOT, MoeError, lib,
 )
 from .ops import (  # noqa: F401
-    Grouping, Layer, bytes_requested, expert_dedup, expert_perslot, kernels_per_call, route_group,
+    Grouping, Layer, bytes_requested, expert_dedup, expert_perslot, kernels_per_call, pack_w_down, route_group,
     step_time_model,
 )

@@ -15,6 +15,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_KIND_SLOT, MOE_KIND_DEDUP = 0, 1
 MOE_MAX_SLOTS, MOE_MAX_TOKENS, MOE_MAX_EXPERTS = 256, 64, 1024
 MOE_FLAG_ACCUMULATE = 1
+MOE_FLAG_WDOWN_PACKED = 2
 MOE_STEP_NMAX, MOE_STEP_AMAX = 16, 64
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_E_INVAL", -2: "MOE_E_DTYPE", -3: "MOE_E_WORKSPACE",
@@ -23,7 +24,7 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_E_INVAL", -2: "MOE_E_DTYPE", -3: "MOE_E_WO
 # every symbol the header declares
 EXPORTS = ("moe_route_group", "moe_workspace_bytes", "moe_expert_perslot", "moe_expert_dedup",
            "moe_kernels_per_call", "moe_expert_perslot_ev", "moe_expert_dedup_ev", "bytes_requested",
-           "step_time_model")
+           "step_time_model", "moe_pack_w_down")
 
 
 class MoeError(RuntimeError):
@@ -93,6 +94,8 @@ def lib():
             L.bytes_requested.restype = i64
             L.step_time_model.argtypes = [ctypes.POINTER(StepIn), ctypes.POINTER(StepOut)]
             L.step_time_model.restype = ctypes.c_int
+            L.moe_pack_w_down.argtypes = [pdesc, vp, vp, vp]
+            L.moe_pack_w_down.restype = ctypes.c_int
             _LIB = L
     return _LIB
 

@@ -160,6 +160,31 @@ struct Steps {
     }
 };
 
+// W_down packed in blocks of 8 columns, [N][d_ff/8][d_model][8] (element (i, f) at
+// byte ((f/8)*d + i)*8*E + (f%8)*E): the 8*k-th .. 8*k+7-th hidden columns of all
+// output rows are contiguous.  Offsets of this lane's 16-byte chunk of row i at wave
+// step i of the d_ff contraction.  With KF the step offset is a scalar offset
+// (d_ff a multiple of the step: it never passes the matrix); otherwise the chunk
+// is formed in the vector offset and checked against d_ff.
+template <bool BF16, bool KF>
+struct PSteps {
+    using F = Fmt<BF16>;
+    int s0, ns, K, d, q;
+    __device__ uint32_t lane_base(bool ok, int row) const {
+        if (!ok) return kOOB;
+        const uint32_t f = (uint32_t)q * F::kPer;  // this lane's columns within a step
+        return ((f / 8) * (uint32_t)d + (uint32_t)row) * 8u * F::kEsize + (f % 8) * F::kEsize;
+    }
+    __device__ uint32_t vofs(uint32_t lb, int i) const {
+        if (KF) return i < ns ? lb : kOOB;
+        const int k = (s0 + i) * F::kStep + q * F::kPer;
+        return (i < ns && k < K) ? cat(lb, (uint32_t)(s0 + i) * 64u * (uint32_t)d) : kOOB;
+    }
+    __device__ uint32_t sofs(int i) const {
+        return (KF && i < ns) ? (uint32_t)(s0 + i) * 64u * (uint32_t)d : 0u;
+    }
+};
+
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
     if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
@@ -479,7 +504,7 @@ constexpr int kSL = 4;  // register mode: h staging loads in flight per thread
 
 // The per-slot kernel holds its registers to 4 waves per SIMD, so that a small
 // pass's gate/up and down work groups are all resident at once.
-template <bool BF16, int MODE, int NT, int RB, bool KF, bool DPF>
+template <bool BF16, int MODE, int NT, int RB, bool KF, bool DPF, bool PK>
 __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(Args a) {
     using F = Fmt<BF16>;
     // ring depth in steps: operand registers per step are (2*RB + NT) for gate/up
@@ -580,13 +605,20 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
             const int S = (a.d_ff + F::kStep - 1) / F::kStep;
             const int s0 = wave * S / kWaves;
             const Steps<BF16, KF> st{s0, (wave + 1) * S / kWaves - s0, a.d_ff, q};
+            const PSteps<BF16, KF> pst{s0, st.ns, a.d_ff, a.d, q};  // W_down packed (PK)
             const int ns = st.ns;
             uint32_t lrow[RB2];
 #pragma unroll
             for (int rb = 0; rb < RB2; ++rb) {
                 const int row = t * RT2 + rb * kTile + lr;
-                lrow[rb] = st.lane_base(row < a.d ? (uint32_t)row * a.d_ff * F::kEsize : kOOB);
+                lrow[rb] = PK ? pst.lane_base(row < a.d, row)
+                              : st.lane_base(row < a.d ? (uint32_t)row * a.d_ff * F::kEsize : kOOB);
             }
+            // W_down chunk of row block rb at wave step j
+            auto wload = [&](int rb, int j) {
+                return PK ? bload2<0>(rd, pst.vofs(lrow[rb], j), pst.sofs(j))
+                          : bload2<0>(rd, st.vofs(lrow[rb], j), st.sofs(j));
+            };
             if constexpr (DPF) {
                 // All of this wave's W_down rows go to registers before the wait, so
                 // they stream from HBM while gate/up items still run.  After the
@@ -596,11 +628,9 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
                 extern __shared__ __align__(16) char hs[];  // [gl][hi row, lo row], padded rows
                 u32x4 pa[kPF][RB2];
 #pragma unroll
-                for (int i = 0; i < kPF; ++i) {
-                    const uint32_t so = st.sofs(i);
+                for (int i = 0; i < kPF; ++i)
 #pragma unroll
-                    for (int rb = 0; rb < RB2; ++rb) pa[i][rb] = bload2<0>(rd, st.vofs(lrow[rb], i), so);
-                }
+                    for (int rb = 0; rb < RB2; ++rb) pa[i][rb] = wload(rb, i);
                 if (tid == 0 && !wait_count(hcnt, a.T1) && a.info) a.info[2] = MOE_E_HIP;
                 __syncthreads();  // h loads (sc1) below are issued after the count was seen
                 const auto rhl = rsrc(a.h, BF16 ? 2 * hbytes : hbytes);  // hi half, then lo half
@@ -673,9 +703,8 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
                 u32x4 ad[P][RB2], bh[P][NT], bl[P][NT];
                 uint32_t lh[NT];
                 auto issue_a = [&](int slot, int j) {
-                    const uint32_t so = st.sofs(j);
 #pragma unroll
-                    for (int rb = 0; rb < RB2; ++rb) ad[slot][rb] = bload2<0>(rd, st.vofs(lrow[rb], j), so);
+                    for (int rb = 0; rb < RB2; ++rb) ad[slot][rb] = wload(rb, j);
                 };
                 auto issue_b = [&](int slot, int j) {
                     const uint32_t so = st.sofs(j);
@@ -792,6 +821,24 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
     }
 }
 
+// Packing of W_down into blocks of 8 columns: dst[e][c][i][k] = src[e][i][8c + k].
+// One thread per 16-byte piece of a source row (8 bf16 or 4 fp32 elements).
+__global__ __launch_bounds__(256) void k_pack_wdown(const char* __restrict__ src, char* __restrict__ dst, int64_t N,
+                                                   int d, int d_ff, int es) {
+    const int per = 16 / es;
+    const int64_t prow = d_ff / per;  // pieces per source row
+    const int64_t pieces = N * d * prow;
+    for (int64_t gi = blockIdx.x * 256ll + threadIdx.x; gi < pieces; gi += (int64_t)gridDim.x * 256) {
+        const int64_t row = gi / prow;  // e*d + i
+        const int f = (int)(gi - row * prow) * per;
+        const int64_t e = row / d;
+        const int i = (int)(row - e * d);
+        const int64_t so = (row * d_ff + f) * es;
+        const int64_t dofs = (((e * (d_ff / 8) + f / 8) * d + i) * 8 + f % 8) * es;
+        *reinterpret_cast<u32x4*>(dst + dofs) = *reinterpret_cast<const u32x4*>(src + so);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Grouping: histogram, exclusive scan and stable scatter of slot indices by
 // expert id, in one workgroup of 256 threads (n*m <= 256, N <= 1024).
@@ -894,7 +941,7 @@ int check_desc(const moe_layer_desc* d, int32_t n) {
     if (d->d_model < 8 || d->d_ff < 8 || (d->d_model % 8) || (d->d_ff % 8)) return MOE_E_DTYPE;
     if (d->N < 1 || d->N > MOE_MAX_EXPERTS || d->m < 1 || d->m > d->N) return MOE_E_INVAL;
     if (n < 1 || n > MOE_MAX_TOKENS || (int64_t)n * d->m > MOE_MAX_SLOTS) return MOE_E_INVAL;
-    if (d->flags & ~MOE_FLAG_ACCUMULATE) return MOE_E_INVAL;
+    if (d->flags & ~(MOE_FLAG_ACCUMULATE | MOE_FLAG_WDOWN_PACKED)) return MOE_E_INVAL;
     const int64_t es = d->dtype == MOE_BF16 ? 2 : 4;
     // one expert matrix must be addressable by a 31-bit buffer offset
     if ((int64_t)d->d_model * d->d_ff * es > (1ll << 31) - 4096) return MOE_E_INVAL;
@@ -953,18 +1000,26 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     return p;
 }
 
-template <bool BF16, int MODE, int NT, int RB>
-void launch(const Args& args, const Plan& p, int grid, hipStream_t st) {
+template <bool BF16, int MODE, int NT, int RB, bool PK>
+void launch_pk(const Args& args, const Plan& p, int grid, hipStream_t st) {
     constexpr int step = Fmt<BF16>::kStep;
     const bool kf = args.d % step == 0 && args.d_ff % step == 0;
     if (kf && p.dpf)
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, true>), dim3(grid), dim3(kThreads), p.lds, st, args);
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, true, PK>), dim3(grid), dim3(kThreads), p.lds, st,
+                           args);
     else if (kf)
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, false>), dim3(grid), dim3(kThreads), 0, st, args);
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, false, PK>), dim3(grid), dim3(kThreads), 0, st, args);
     else if (p.dpf)
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, true>), dim3(grid), dim3(kThreads), p.lds, st, args);
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, true, PK>), dim3(grid), dim3(kThreads), p.lds, st,
+                           args);
     else
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, false>), dim3(grid), dim3(kThreads), 0, st, args);
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, false, PK>), dim3(grid), dim3(kThreads), 0, st, args);
+}
+
+template <bool BF16, int MODE, int NT, int RB>
+void launch(const Args& args, const Plan& p, int grid, hipStream_t st, bool packed) {
+    if (packed) launch_pk<BF16, MODE, NT, RB, true>(args, p, grid, st);
+    else launch_pk<BF16, MODE, NT, RB, false>(args, p, grid, st);
 }
 
 template <int MODE>
@@ -1016,14 +1071,15 @@ int run_expert(const moe_layer_desc* d, const moe_layer_weights* W, const void* 
     (void)hipGetLastError();
     if (events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(events[0]), st);
     const bool bf = d->dtype == MOE_BF16;
+    const bool pk = (d->flags & MOE_FLAG_WDOWN_PACKED) != 0;
     if (bf) {
-        if (p.nt == 1) launch<true, MODE, 1, 2>(args, p, grid, st);
-        else if (p.nt == 2) launch<true, MODE, 2, 2>(args, p, grid, st);
-        else launch<true, MODE, 4, 1>(args, p, grid, st);
+        if (p.nt == 1) launch<true, MODE, 1, 2>(args, p, grid, st, pk);
+        else if (p.nt == 2) launch<true, MODE, 2, 2>(args, p, grid, st, pk);
+        else launch<true, MODE, 4, 1>(args, p, grid, st, pk);
     } else {
-        if (p.nt == 1) launch<false, MODE, 1, 2>(args, p, grid, st);
-        else if (p.nt == 2) launch<false, MODE, 2, 2>(args, p, grid, st);
-        else launch<false, MODE, 4, 1>(args, p, grid, st);
+        if (p.nt == 1) launch<false, MODE, 1, 2>(args, p, grid, st, pk);
+        else if (p.nt == 2) launch<false, MODE, 2, 2>(args, p, grid, st, pk);
+        else launch<false, MODE, 4, 1>(args, p, grid, st, pk);
     }
     if (events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(events[1]), st);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
@@ -1053,6 +1109,27 @@ size_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t n, int32_t kind) 
         total = t > total ? t : total;
     }
     return total;
+}
+
+int moe_pack_w_down(const moe_layer_desc* desc, const void* w_down, void* w_down_packed, void* hip_stream) {
+    if (!desc) return MOE_E_INVAL;
+    moe_layer_desc dd = *desc;
+    dd.flags = 0;
+    const int rc = check_desc(&dd, 1);
+    if (rc != MOE_OK) return rc;
+    if (!w_down || !w_down_packed || !aligned16(w_down) || !aligned16(w_down_packed)) return MOE_E_INVAL;
+    const int64_t es = desc->dtype == MOE_BF16 ? 2 : 4;
+    const int64_t bytes = (int64_t)desc->N * desc->d_model * desc->d_ff * es;
+    const char* a0 = reinterpret_cast<const char*>(w_down);
+    const char* b0 = reinterpret_cast<const char*>(w_down_packed);
+    if (a0 < b0 + bytes && b0 < a0 + bytes) return MOE_E_INVAL;  // overlapping
+    const int64_t pieces = bytes / 16;
+    const int grid = (int)std::min<int64_t>((pieces + 255) / 256, 65536);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_pack_wdown, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(hip_stream),
+                       reinterpret_cast<const char*>(w_down), reinterpret_cast<char*>(w_down_packed),
+                       (int64_t)desc->N, desc->d_model, desc->d_ff, (int)es);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 
 int moe_kernels_per_call(int32_t kind) {

@@ -44,21 +44,36 @@ def _check_dev(name, t, dtype=None, shape=None):
 
 
 class Layer:
-    """Device weights of one MoE layer: W_gate, W_up [N][d_ff][d], W_down [N][d][d_ff]."""
+    """Device weights of one MoE layer: W_gate, W_up [N][d_ff][d], W_down [N][d][d_ff],
+    or, with ``packed``, W_down in the layout of ``moe_pack_w_down``,
+    [N][d_ff/8][d][8] (see ``Layer.packed_copy``)."""
 
-    def __init__(self, w_gate, w_up, w_down, m):
+    def __init__(self, w_gate, w_up, w_down, m, packed=False):
         N, d_ff, d = w_gate.shape
         _check_dev("w_gate", w_gate)
         _check_dev("w_up", w_up, w_gate.dtype, (N, d_ff, d))
-        _check_dev("w_down", w_down, w_gate.dtype, (N, d, d_ff))
+        if packed:
+            _check_dev("w_down", w_down, w_gate.dtype, (N, d_ff // 8, d, 8))
+        else:
+            _check_dev("w_down", w_down, w_gate.dtype, (N, d, d_ff))
         self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
         self.N, self.m, self.d, self.d_ff = N, int(m), d, d_ff
         self.dtype = w_gate.dtype
+        self.packed = bool(packed)
         self._weights = _abi.LayerWeights(w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr())
 
     def desc(self, accumulate=False):
-        return _abi.LayerDesc(self.N, self.m, self.d, self.d_ff, _dtype_code(self.w_gate),
-                              _abi.MOE_FLAG_ACCUMULATE if accumulate else 0)
+        flags = (_abi.MOE_FLAG_ACCUMULATE if accumulate else 0) | (_abi.MOE_FLAG_WDOWN_PACKED if self.packed else 0)
+        return _abi.LayerDesc(self.N, self.m, self.d, self.d_ff, _dtype_code(self.w_gate), flags)
+
+    def packed_copy(self, stream=None):
+        """The same layer with W_down packed by ``moe_pack_w_down`` (a new device tensor;
+        W_gate and W_up shared)."""
+        if self.packed:
+            return self
+        dst = torch.empty((self.N, self.d_ff // 8, self.d, 8), dtype=self.dtype, device=self.w_down.device)
+        pack_w_down(self, self.w_down, dst, stream=stream)
+        return Layer(self.w_gate, self.w_up, dst, self.m, packed=True)
 
     @property
     def expert_bytes(self):
@@ -70,6 +85,15 @@ class Layer:
         if nb == 0:
             raise _abi.MoeError("moe_workspace_bytes", _abi.MOE_E_INVAL)
         return torch.zeros(nb, dtype=torch.uint8, device=self.w_gate.device)
+
+
+def pack_w_down(layer, w_down, out, stream=None):
+    """Copy W_down [N][d][d_ff] into the packed layout [N][d_ff/8][d][8] (one launch)."""
+    _check_dev("w_down", w_down, layer.dtype, (layer.N, layer.d, layer.d_ff))
+    _check_dev("out", out, layer.dtype, (layer.N, layer.d_ff // 8, layer.d, 8))
+    desc = _abi.LayerDesc(layer.N, layer.m, layer.d, layer.d_ff, _dtype_code(layer.w_gate), 0)
+    check("moe_pack_w_down", lib().moe_pack_w_down(ctypes.byref(desc), _vp(w_down), _vp(out), _stream(stream)))
+    return out
 
 
 def route_group(ids, N, out=None, stream=None):

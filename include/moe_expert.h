@@ -28,6 +28,7 @@
  *     all accumulation is fp32; y is fp32.
  *   - Weight layouts, row-major and contiguous:
  *         W_gate, W_up : [N][d_ff][d_model]      W_down : [N][d_model][d_ff]
+ *     (or W_down packed by moe_pack_w_down, flagged MOE_FLAG_WDOWN_PACKED);
  *     x : [n][d_model];  ids : [n][m] int32;  w : [n][m] fp32;  y : [n][d_model].
  *   - Workspaces (`ws`) are caller-owned device memory that must be zero-filled
  *     once before first use (e.g. hipMemset); every call that runs to completion
@@ -61,6 +62,8 @@ enum { MOE_KIND_SLOT = 0, MOE_KIND_DEDUP = 1 };
 #define MOE_MAX_TOKENS 64     /* n */
 #define MOE_MAX_EXPERTS 1024  /* N */
 #define MOE_FLAG_ACCUMULATE 1u /* y += result (else y = result) */
+/* w_down is in the packed layout of moe_pack_w_down (else [N][d_model][d_ff]) */
+#define MOE_FLAG_WDOWN_PACKED 2u
 
 /* One MoE layer.  1 <= m <= N (m == N is allowed so that always-on shared
  * experts can run as a layer whose every token selects all of them). */
@@ -146,6 +149,23 @@ int moe_expert_perslot(const moe_layer_desc* desc, const moe_layer_weights* weig
 int moe_expert_dedup(const moe_layer_desc* desc, const moe_layer_weights* weights, const void* x,
                      const int32_t* ids, const float* w, int32_t n, float* y, int32_t* info,
                      void* ws, size_t ws_bytes, void* hip_stream);
+
+/*
+ * moe_pack_w_down -- copy W_down [N][d_model][d_ff] into the packed layout
+ * [N][d_ff/8][d_model][8]: element (e, i, f) goes to
+ *     ((e*(d_ff/8) + f/8)*d_model + i)*8 + f%8,
+ * so that every run of 8 hidden columns of all output rows is contiguous (a
+ * block of d_ff rows then reads its down-projection columns in whole cache lines
+ * instead of 16- to 64-byte pieces of every output row).  Same byte size as the
+ * source.  Expert calls read W_down in this layout when desc->flags has
+ * MOE_FLAG_WDOWN_PACKED, in the same kernels and with the same result as the plain
+ * layout (the down items' loads become whole-line reads).  A weight-load-time step,
+ * not part of the expert operation.
+ *   w_down, w_down_packed  device, 16-byte aligned, not overlapping; desc->flags ignored.
+ * Asynchronous on hip_stream.  Returns MOE_OK, MOE_E_INVAL / MOE_E_DTYPE for bad
+ * arguments (nothing enqueued), or MOE_E_HIP. */
+int moe_pack_w_down(const moe_layer_desc* desc, const void* w_down, void* w_down_packed,
+                    void* hip_stream);
 
 /* Number of kernel launches moe_expert_perslot / moe_expert_dedup enqueue per
  * call (moe_route_group is a separate, optional launch), or a negative status for

@@ -24,10 +24,13 @@ def say(*a):
 class DeviceLayer:
     """Host weights (for the oracle) and their device copy (for the kernels)."""
 
-    def __init__(self, spec, seed, layer=0, with_shared=False, host=None):
+    def __init__(self, spec, seed, layer=0, with_shared=False, host=None, packed=False):
         self.spec = spec
         self.host = host if host is not None else synth.layer_weights(spec, seed, layer)
         self.dev = efa.Layer(*(to_torch(a) for a in self.host), m=spec.m)
+        if packed:  # W_down in the packed layout (moe_pack_w_down); the plain copy is dropped
+            self.dev = self.dev.packed_copy()
+            torch.cuda.synchronize()
         self.shared_host = None
         self.shared_dev = None
         if with_shared and spec.n_shared:

@@ -74,11 +74,32 @@ def _compare(dl, x, ids, w, what, shared=False, tokens=None):
     return r1, r2
 
 
-def test_tiny_fp32_many_seeds():
+@pytest.mark.parametrize("dtype,shape", [("bf16", (3, 64, 40)), ("bf16", (5, 2048, 1408)), ("f32", (4, 72, 136)),
+                                          ("f32", (2, 32, 8))])
+def test_pack_w_down_bit_exact(dtype, shape):
+    """moe_pack_w_down against the layout definition: packed[e][c][i][k] = W[e][i][8c + k]."""
+    say("pack", dtype, shape)
+    N, d, d_ff = shape
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    wd = torch.randn(N, d, d_ff, generator=g, device="cuda").to(tdt)
+    wg = torch.zeros(N, d_ff, d, dtype=tdt, device="cuda")
+    layer = efa.Layer(wg, wg, wd, m=1)
+    out = torch.full((N, d_ff // 8, d, 8), 7, dtype=tdt, device="cuda")
+    efa.pack_w_down(layer, wd, out)
+    torch.cuda.synchronize()
+    ref = wd.cpu().reshape(N, d, d_ff // 8, 8).permute(0, 2, 1, 3).contiguous()
+    assert torch.equal(out.cpu().view(torch.int16 if dtype == "bf16" else torch.int32),
+                       ref.view(torch.int16 if dtype == "bf16" else torch.int32))
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_tiny_fp32_many_seeds(packed):
     spec = synth.CONFIGS["tiny"]
-    for seed in range(30):
-        say("tiny seed", seed)
-        dl = DeviceLayer(spec, seed)
+    for seed in range(30 if not packed else 10):
+        say("tiny seed", seed, "packed", packed)
+        dl = DeviceLayer(spec, seed, packed=packed)
         tr = routing.uniform_trace(spec.N, spec.m, 4, routing.rng_for(seed, 0, "uniform"))
         x = synth.pass_x(spec, seed, 0, 0, 4)
         (rel, mx), _ = _compare(dl, x, tr.ids, tr.w, "tiny seed %d" % seed)
@@ -92,19 +113,24 @@ def test_tiny_fp32_many_seeds():
     # d_ff too long for the down weights to sit in registers: the streaming down path
     (7, 2, 136, 1560, 5), (7, 2, 136, 1560, 40),
     # 128..1024 gate/up tiles: K ranges shared between work groups (split tiles)
-    (40, 4, 72, 1000, 3), (40, 4, 200, 520, 5)])
-def test_ragged_shapes(dtype, N, m, d, d_ff, n):
-    say("ragged", dtype, N, m, d, d_ff, n)
+    (40, 4, 72, 1000, 3), (40, 4, 200, 520, 5),
+    # multiples of 32: the fused pass with packed W_down (n <= 8), several shares per unit
+    # and units per share, blocks cut by share boundaries
+    (6, 3, 96, 160, 1), (6, 3, 96, 160, 8), (33, 8, 256, 64, 7), (4, 4, 64, 96, 8), (12, 6, 512, 352, 5)])
+@pytest.mark.parametrize("packed", [False, True])
+def test_ragged_shapes(dtype, N, m, d, d_ff, n, packed):
+    say("ragged", dtype, N, m, d, d_ff, n, "packed", packed)
     spec = synth.layer_spec("tiny", N=N, m=m, d=d, d_ff=d_ff, dtype=dtype, sigma=0.05)
-    dl = DeviceLayer(spec, 17)
+    dl = DeviceLayer(spec, 17, packed=packed)
     tr = routing.correlated_trace(N, m, n, 0.7, routing.rng_for(17, 0, "correlated"))
     x = synth.pass_x(spec, 17, 0, 1, n)
     _compare(dl, x, tr.ids, tr.w, "ragged")
 
 
-def test_max_reuse_and_no_reuse():
+@pytest.mark.parametrize("packed", [False, True])
+def test_max_reuse_and_no_reuse(packed):
     spec = synth.layer_spec("tiny", N=70, m=4, d=128, d_ff=96, dtype="bf16")
-    dl = DeviceLayer(spec, 3)
+    dl = DeviceLayer(spec, 3, packed=packed)
     rng = np.random.default_rng(3)
     for n in (1, 8, 16, 17, 32, 33, 64):
         say("max reuse n", n)
@@ -119,9 +145,10 @@ def test_max_reuse_and_no_reuse():
     _compare(dl, synth.pass_x(spec, 3, 0, 99, 17), ids, w, "no reuse")
 
 
-def test_invalid_ids_skip_slot_and_flag():
+@pytest.mark.parametrize("packed", [False, True])
+def test_invalid_ids_skip_slot_and_flag(packed):
     spec = synth.layer_spec("tiny", N=8, m=2, d=64, d_ff=64, dtype="bf16")
-    dl = DeviceLayer(spec, 5)
+    dl = DeviceLayer(spec, 5, packed=packed)
     ids = np.array([[0, 3], [5, 9], [2, 1]], np.int32)   # slot (1,1) out of range
     w = np.array([[0.5, 0.5], [0.7, 0.3], [0.6, 0.4]], np.float32)
     x = synth.pass_x(spec, 5, 0, 0, 3)
@@ -138,9 +165,10 @@ def test_invalid_ids_skip_slot_and_flag():
     _agree(ys, yd, "invalid")
 
 
-def test_accumulate_and_determinism():
+@pytest.mark.parametrize("packed", [False, True])
+def test_accumulate_and_determinism(packed):
     spec = synth.layer_spec("tiny", N=16, m=4, d=256, d_ff=128, dtype="bf16")
-    dl = DeviceLayer(spec, 8)
+    dl = DeviceLayer(spec, 8, packed=packed)
     tr = routing.uniform_trace(16, 4, 6, routing.rng_for(8, 0, "uniform"))
     x = synth.pass_x(spec, 8, 0, 0, 6)
     say("determinism")
@@ -167,8 +195,18 @@ def dsv2():
     return DeviceLayer(synth.CONFIGS["dsv2lite"], 2026, with_shared=True)
 
 
+@pytest.fixture(scope="module")
+def dsv2p(dsv2):
+    """The same layer with W_down packed."""
+    say("pack dsv2lite layer")
+    dl = DeviceLayer(dsv2.spec, 2026, with_shared=True, host=dsv2.host, packed=True)
+    return dl
+
+
 @pytest.mark.parametrize("kind", ["uniform", "correlated"])
-def test_dsv2lite_windows(dsv2, kind):
+@pytest.mark.parametrize("packed", [False, True])
+def test_dsv2lite_windows(dsv2, dsv2p, kind, packed):
+    dsv2 = dsv2p if packed else dsv2
     spec = dsv2.spec
     tr = routing.make_trace(spec, kind, 512, seed=2026, p=0.5)
     starts = routing.window_starts(512, 8, 8, seed=2026)
@@ -180,10 +218,11 @@ def test_dsv2lite_windows(dsv2, kind):
         _compare(dsv2, x, ids, w, "dsv2lite %s n=%d" % (kind, n), shared=(n in (1, 5)))
 
 
-def test_qwen3_layer_zipf_and_tree():
+@pytest.mark.parametrize("packed", [False, True])
+def test_qwen3_layer_zipf_and_tree(packed):
     spec = synth.CONFIGS["qwen3"]
-    say("upload qwen3 layer")
-    dl = DeviceLayer(spec, 77, layer=3)
+    say("upload qwen3 layer", "packed", packed)
+    dl = DeviceLayer(spec, 77, layer=3, packed=packed)
     tr = routing.make_trace(spec, "zipf", 256, seed=77, layer=3, s=1.1)
     for n in (1, 2, 4, 8):
         ids, w = routing.window(tr, 5 * n, n)
@@ -196,10 +235,11 @@ def test_qwen3_layer_zipf_and_tree():
     _compare(dl, x, ttr.ids, ttr.w, "tree", tokens=[0, 1, 7, 19, 31])
 
 
-def test_mixtral_sampled_tokens():
+@pytest.mark.parametrize("packed", [False, True])
+def test_mixtral_sampled_tokens(packed):
     spec = synth.CONFIGS["mixtral"]
-    say("upload mixtral layer")
-    dl = DeviceLayer(spec, 9)
+    say("upload mixtral layer", "packed", packed)
+    dl = DeviceLayer(spec, 9, packed=packed)
     tr = routing.make_trace(spec, "correlated", 64, seed=9, p=0.6)
     for n, toks in ((1, [0]), (3, [0, 2]), (8, [1, 6])):
         ids, w = routing.window(tr, 10, n)
@@ -209,11 +249,13 @@ def test_mixtral_sampled_tokens():
 
 
 @pytest.mark.parametrize("kind", ["uniform", "correlated"])
-def test_repeated_passes_bitwise_stable(dsv2, kind):
+@pytest.mark.parametrize("packed", [False, True])
+def test_repeated_passes_bitwise_stable(dsv2, dsv2p, kind, packed):
     """Many back-to-back passes on one workspace, per-slot and dedup alternating:
     every result bitwise equal to the first of its kind, the two kinds equal to
     summation order.  Data handed between workgroups (h, O, partial sums) that
     were not yet visible, or counters not reset between calls, would break it."""
+    dsv2 = dsv2p if packed else dsv2
     spec = dsv2.spec
     tr = routing.make_trace(spec, kind, 256, seed=31, p=0.5)
     ws = dsv2.dev.workspace(8)
@@ -234,3 +276,44 @@ def test_repeated_passes_bitwise_stable(dsv2, kind):
             assert torch.equal(o, refs[it % 2]), (n, it)
         _agree(refs[0].cpu().numpy(), refs[1].cpu().numpy(), "repeat n=%d" % n)
         assert int(info[2].item()) == 0
+
+
+def test_packed_and_plain_agree(dsv2, dsv2p):
+    """The same passes with plain and packed W_down (the fused pass for n <= 8) agree to
+    fp32 summation order."""
+    spec = dsv2.spec
+    tr = routing.make_trace(spec, "correlated", 256, seed=5, p=0.5)
+    for n in (1, 2, 5, 8, 9):
+        ids_h, w_h = routing.window(tr, 3 * n, n)
+        x = synth.pass_x(spec, 5, 0, n, n)
+        say("plain vs packed n", n)
+        a = dsv2.run(x, ids_h, w_h)
+        b = dsv2p.run(x, ids_h, w_h)
+        _agree(a[0], b[0], "perslot plain/packed n=%d" % n)
+        _agree(a[1], b[1], "dedup plain/packed n=%d" % n)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_repeated_ids_count_as_often_as_they_appear(packed):
+    """An id repeated within a token (flagged MOE_E_IDS) counts as often as it appears in
+    both kernels; with 8 tokens listing one expert 4 times its group has 32 slots, more
+    than one 16-column tile."""
+    spec = synth.layer_spec("tiny", N=20, m=4, d=128, d_ff=96, dtype="bf16")
+    dl = DeviceLayer(spec, 4, packed=packed)
+    rng = np.random.default_rng(4)
+    ids = np.stack([rng.choice(spec.N, spec.m, replace=False) for _ in range(8)]).astype(np.int32)
+    ids[:, :] = 3
+    ids[2, 1] = 7
+    w = rng.random((8, spec.m)).astype(np.float32)
+    x = synth.pass_x(spec, 4, 0, 0, 8)
+    say("repeated ids packed", packed)
+    ys, yd, info = dl.run(x, ids, w)
+    assert info[1] == efa._abi.MOE_E_IDS and info[0] == 2
+    _agree(ys, yd, "repeated ids")
+    # the same sums with each repeat folded into one slot of summed weight
+    ids1 = np.array([[3, 7] if t == 2 else [3, 5] for t in range(8)], np.int32)
+    w1 = np.array([[w[t, 0] + w[t, 2] + w[t, 3], w[t, 1]] if t == 2 else [w[t].sum(), 0.0] for t in range(8)],
+                  np.float32)
+    ref = oracle.moe_ffn(*dl.host, x, ids1, w1, "bf16")
+    assert_close(ys, ref, "repeated ids perslot")
+    assert_close(yd, ref, "repeated ids dedup")
