@@ -542,7 +542,26 @@ def main():
                 efa.expert_dedup(shl, x, sids, sw, y=ys[n], ws=sws, stream=stream, events=e2)
                 tl.append(ev.ms(e2[0], e2[1]) * 1e3)
             shared_us.append(sorted(tl[1:])[1])
-        del shl
+        # the same experts computed in the routed call itself (one launch): routed
+        # alone and routed + shared on the same windows, paired, both kernels
+        fl = efa.Layer(layer.w_gate, layer.w_up, layer.w_down, m=spec.m, packed=layer.packed,
+                       shared=(shl.w_gate, shl.w_up, shl.w_down))
+        fws = fl.workspace(nvals[-1])
+        fused = {"routed_slot": [], "fused_slot": [], "routed_dedup": [], "fused_dedup": []}
+        for n in nvals:
+            for kname, fn in (("slot", efa.expert_perslot), ("dedup", efa.expert_dedup)):
+                tr_, tf_ = [], []
+                for s_ in range(min(4, nsteps_total)):
+                    p = passes[(kinds[0][0], n, s_)]
+                    flush()
+                    fn(layer, p["x"], p["ids"], p["w"], y=ys[n], ws=ws, stream=stream, events=e2)
+                    tr_.append(ev.ms(e2[0], e2[1]) * 1e3)
+                    flush()
+                    fn(fl, p["x"], p["ids"], p["w"], y=ys[n], ws=fws, stream=stream, events=e2)
+                    tf_.append(ev.ms(e2[0], e2[1]) * 1e3)
+                fused["routed_" + kname].append(round(float(np.median(tr_)), 2))
+                fused["fused_" + kname].append(round(float(np.median(tf_)), 2))
+        del shl, fl, fws
 
     # aggregate (bytes and times summed over the timed passes)
     per_kind = {}
@@ -550,6 +569,11 @@ def main():
         rows = per_n_rows([r for r in recs if r["kind"] == kind], nvals)
         per_kind[kind] = dict(per_n=strip_bytes(rows), crossover=crossover_of(rows),
                               step_model=step_model_section(efa, spec, rows, shared_us))
+        if spec.n_shared:
+            # D/beta_D from the time the shared experts add to the routed launch
+            marg = [f - r for k in ("slot", "dedup") for f, r in zip(fused["fused_" + k], fused["routed_" + k])]
+            per_kind[kind]["step_model_shared_in_call"] = step_model_section(
+                efa, spec, rows, [max(sum(marg) / len(marg), 1e-3)])
 
     tot_bytes = sum(r["bytes_slot"] + r["bytes_dedup"] for r in recs)
     tot_s = sum(r["t_slot_ms"] + r["t_dedup_ms"] for r in recs) / 1e3
@@ -579,7 +603,11 @@ def main():
         extras["shared_experts"] = {"workload": "%d always-on shared experts, weight 1, every token: one "
                                                 "deduplicating call per pass (the D(n) bytes of the step model)"
                                                 % spec.n_shared, "us_per_n": [round(v, 2) for v in shared_us],
-                                    "bytes": spec.n_shared * spec.expert_bytes}
+                                    "bytes": spec.n_shared * spec.expert_bytes,
+                                    "in_call": dict(workload="the same experts computed in the routed launch "
+                                                             "(desc n_shared); routed alone vs routed + shared, "
+                                                             "paired on %s windows, median of 4" % kinds[0][0],
+                                                    **{k + "_us": v for k, v in fused.items()})}
     if not args.no_extras and args.config == "dsv2lite":
         del passes, layer
         torch.cuda.empty_cache()

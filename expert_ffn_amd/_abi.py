@@ -13,7 +13,7 @@ SO_PATH = os.path.join(HERE, "libmoe_expert.so")
 MOE_OK, MOE_E_INVAL, MOE_E_DTYPE, MOE_E_WORKSPACE, MOE_E_HIP, MOE_E_IDS = 0, -1, -2, -3, -4, -5
 MOE_F32, MOE_BF16 = 0, 1
 MOE_KIND_SLOT, MOE_KIND_DEDUP = 0, 1
-MOE_MAX_SLOTS, MOE_MAX_TOKENS, MOE_MAX_EXPERTS = 256, 64, 1024
+MOE_MAX_SLOTS, MOE_MAX_TOKENS, MOE_MAX_EXPERTS, MOE_MAX_SHARED = 256, 64, 1024, 16
 MOE_FLAG_ACCUMULATE = 1
 MOE_FLAG_WDOWN_PACKED = 2
 MOE_STEP_NMAX, MOE_STEP_AMAX = 16, 64
@@ -35,11 +35,14 @@ class MoeError(RuntimeError):
 
 class LayerDesc(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int32), ("m", ctypes.c_int32), ("d_model", ctypes.c_int32),
-                ("d_ff", ctypes.c_int32), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("d_ff", ctypes.c_int32), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("n_shared", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
-    _fields_ = [("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p)]
+    _fields_ = [("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("w_gate_shared", ctypes.c_void_p), ("w_up_shared", ctypes.c_void_p),
+                ("w_down_shared", ctypes.c_void_p)]
 
 
 _NM, _AM = MOE_STEP_NMAX, MOE_STEP_AMAX

@@ -205,23 +205,35 @@ __device__ __forceinline__ int atomic_load_agent(const int32_t* p) {
 struct Args {
     const char* wg;      // W_gate [N][d_ff][d]
     const char* wu;      // W_up   [N][d_ff][d]
-    const char* wd;      // W_down [N][d][d_ff]
+    const char* wd;      // W_down [N][d][d_ff] (or packed)
+    const char* wgs;     // always-on (shared) experts: W_gate [n_shared][d_ff][d], or null
+    const char* wus;     // W_up [n_shared][d_ff][d]
+    const char* wds;     // W_down [n_shared][d][d_ff], layout as wd
     const char* x;       // [n][d]
     const int32_t* ids;  // [n*m]
     const float* w;      // [n*m]
     float* y;            // [n][d]
-    char* h;             // bf16: hi [nm][d_ff] then lo [nm][d_ff]; fp32: [nm][d_ff]
-    float* O;            // [nm][d]
+    char* h;             // bf16: hi [nslot][d_ff] then lo [nslot][d_ff]; fp32: [nslot][d_ff]
+    float* O;            // [nslot][d]
     int32_t* sync;       // counters, see layout above
     int32_t* info;       // optional [3]
     int32_t n, m, N, d, d_ff;
     int32_t units, T1, T2;
+    int32_t units_r;     // routed units; units units_r .. units-1 are the shared experts
+    int32_t n_shared;
+    int32_t nslot;       // rows of h and O: routed slots t*m + j, then shared slots nm + s*n + t
     int32_t accumulate;
     int32_t gl;          // down items in register mode: tokens of h staged in LDS at a time
     int32_t g1;          // gate/up work groups (they take the first g1 block ids)
     int32_t S1;          // K steps of one gate/up row tile
-    float* part;         // split gate/up tiles: partial sums [kMaxContrib][nm][d_ff][gate, up]
+    float* part;         // split gate/up tiles: partial sums [kMaxContrib][nslot][d_ff][gate, up]
 };
+
+// token of a slot: routed slot t*m + j, shared slot n*m + s*n + t
+__device__ __forceinline__ int slot_tok(const Args& a, int slot) {
+    const int nm = a.n * a.m;
+    return slot < nm ? slot / a.m : (slot - nm) % a.n;
+}
 
 template <int NB>
 struct Smem {
@@ -319,9 +331,9 @@ __device__ bool wait_count(const int32_t* p, int target) {
 // contributor order and then its own, and finalises h.  Returns true in the work
 // group that finalised the tile.
 // ---------------------------------------------------------------------------
-template <bool BF16, int NT, int RB, bool KF, int P>
-__device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e, int g, int t, int k0, int k1,
-                                        int tile, int nc, int j) {
+template <bool BF16, int NT, int RB, bool KF, int P, bool SH>
+__device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e, bool sh, int g, int t, int k0,
+                                        int k1, int tile, int nc, int j) {
     using F = Fmt<BF16>;
     constexpr int H = P / 2;        // half ring
     constexpr int RT = kTile * RB;  // output rows of a tile
@@ -333,10 +345,10 @@ __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e,
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, q = lane >> 4;
-    const int nm = a.n * a.m;
+    const int nslot = SH ? a.nslot : a.n * a.m;
     const uint32_t mat = (uint32_t)a.d_ff * a.d * F::kEsize;
-    const auto rg = rsrc(a.wg + (size_t)e * mat, mat);
-    const auto ru = rsrc(a.wu + (size_t)e * mat, mat);
+    const auto rg = rsrc((SH && sh ? a.wgs : a.wg) + (size_t)e * mat, mat);
+    const auto ru = rsrc((SH && sh ? a.wus : a.wu) + (size_t)e * mat, mat);
     const auto rx = rsrc(a.x, (uint32_t)(a.n * a.d * F::kEsize));
     int32_t* tc = a.sync + kLine * (MOE_MAX_SLOTS + kMaxDownTiles + tile);  // split tile: partials stored
     const int len = k1 - k0;
@@ -345,7 +357,7 @@ __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e,
     const int ns = st.ns;
     // h = silu(G) * U for rows f0 .. f0+3 of slot `slot` (bf16: hi and lo halves)
     auto store_h = [&](f32x4 G, f32x4 Uu, int slot, int f0) {
-        const auto rhw = rsrc(a.h, (uint32_t)nm * a.d_ff * 4);  // h region: hi+lo bf16 or fp32
+        const auto rhw = rsrc(a.h, (uint32_t)nslot * a.d_ff * 4);  // h region: hi+lo bf16 or fp32
         const uint32_t idx = (uint32_t)slot * a.d_ff + f0;
         float hv[4];
 #pragma unroll
@@ -357,7 +369,7 @@ __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e,
                 hi[i] = bf16_rne(hv[i]);
                 lo[i] = bf16_rne(hv[i] - bf16_to_f32(hi[i]));
             }
-            const uint32_t half = (uint32_t)nm * a.d_ff * 2;  // bytes of the hi half
+            const uint32_t half = (uint32_t)nslot * a.d_ff * 2;  // bytes of the hi half
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)}, rhw, idx * 2,
                                                   0, kSc1);
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)}, rhw,
@@ -378,7 +390,8 @@ __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e,
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
             const int gi = base + tt * 16 + lr;
-            lx[tt] = st.lane_base(gi < g ? (uint32_t)(sm.grp[gi] / a.m) * a.d * F::kEsize : kOOB);
+            const int tok = gi < g ? (SH ? slot_tok(a, sm.grp[gi]) : sm.grp[gi] / a.m) : 0;
+            lx[tt] = st.lane_base(gi < g ? (uint32_t)tok * a.d * F::kEsize : kOOB);
         }
         u32x4 ag[P][RB], au[P][RB], bx[P][NT];
         auto issue = [&](int slot, int j) {  // loads of wave step j into ring slot `slot`
@@ -446,8 +459,8 @@ __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e,
                     store_h(G, Uu, slot, f0);
                 } else {
                     // partial of contributor jj at jj*pstride + pb: (gate, up) pairs of rows f0 .. f0+3
-                    const auto rp = rsrc(a.part, (uint32_t)kMaxContrib * nm * a.d_ff * 8);
-                    const uint32_t pstride = (uint32_t)nm * a.d_ff * 8;
+                    const auto rp = rsrc(a.part, (uint32_t)kMaxContrib * nslot * a.d_ff * 8);
+                    const uint32_t pstride = (uint32_t)nslot * a.d_ff * 8;
                     const uint32_t pb = ((uint32_t)slot * a.d_ff + f0) * 8;
                     if (j < nc - 1) {
                         __builtin_amdgcn_raw_buffer_store_b128(
@@ -504,7 +517,7 @@ constexpr int kSL = 4;  // register mode: h staging loads in flight per thread
 
 // The per-slot kernel holds its registers to 4 waves per SIMD, so that a small
 // pass's gate/up and down work groups are all resident at once.
-template <bool BF16, int MODE, int NT, int RB, bool KF, bool DPF, bool PK>
+template <bool BF16, int MODE, int NT, int RB, bool KF, bool DPF, bool PK, bool SH>
 __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(Args a) {
     using F = Fmt<BF16>;
     // ring depth in steps: operand registers per step are (2*RB + NT) for gate/up
@@ -524,19 +537,27 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
     const bool phase1 = (int)blockIdx.x < a.g1;
     const bool want_status = a.info != nullptr && blockIdx.x == 0;
 
-    // The unit u: expert e and its slots sm.grp[0..g).  `status`: also report U and
-    // the ids' status (work group 0).
-    auto resolve = [&](int u, bool status, int& e, int& g) {
-        if (MODE == kDedup || status) {
+    // The unit u: expert e and its slots sm.grp[0..g); sh: e is a shared expert (all
+    // n tokens, weight 1, slots nm + e*n + t).  `status`: also report U and the ids'
+    // status (work group 0).
+    auto resolve = [&](int u, bool status, int& e, int& g, bool& sh) {
+        sh = SH && u >= a.units_r;
+        if ((MODE == kDedup && !sh) || status) {
             int U;
-            group_prologue<NT * RB>(a, sm, MODE == kDedup ? u : 0, status, MODE == kDedup, e, g, U);
+            group_prologue<NT * RB>(a, sm, MODE == kDedup && !sh ? u : 0, status, MODE == kDedup && !sh, e, g, U);
             if (status && tid == 0) {
                 a.info[0] = U;
                 a.info[1] = sm.meta[3] ? MOE_E_IDS : MOE_OK;
                 a.info[2] = MOE_OK;  // a bounded wait that expires later overwrites this
             }
         }
-        if (MODE == kDedup) {
+        if (sh) {
+            e = u - a.units_r;
+            g = a.n;
+            __syncthreads();  // the previous unit's reads of sm.grp are done
+            if (tid < a.n) sm.grp[tid] = nm + e * a.n + tid;
+            __syncthreads();
+        } else if (MODE == kDedup) {
             e = uni(e);
             g = uni(g);
         } else {
@@ -568,6 +589,7 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
         // order no wait depends on another wait.
         const int lbeg = uni(split ? wi * ltot / a.g1 : wi * a.S1);
         int cur = -1, e = -1, g = 0;
+        bool sh = false;
         for (int L = uni(split ? (wi + 1) * ltot / a.g1 : (wi + 1) * a.S1); L > lbeg;) {
             const int tile = uni((L - 1) / a.S1);
             const int k1 = L - tile * a.S1;
@@ -575,17 +597,18 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
             L = tile * a.S1 + k0;
             const int u = uni(tile / a.T1), t = tile - u * a.T1;
             if (u != cur) {
-                resolve(u, want_status && cur < 0, e, g);
+                resolve(u, want_status && cur < 0, e, g, sh);
                 cur = u;
             }
             if (g == 0) continue;
             // work groups whose shares meet this tile: first .. last
             const int first = uni(split ? ((tile * a.S1 + 1) * a.g1 - 1) / ltot : wi);
             const int last = uni(split ? ((tile * a.S1 + a.S1) * a.g1 - 1) / ltot : wi);
-            const bool fin = gate_up<BF16, NT, RB, KF, P>(a, sm, e, g, t, k0, k1, tile, last - first + 1, wi - first);
+            const bool fin = gate_up<BF16, NT, RB, KF, P, SH>(a, sm, e, sh, g, t, k0, k1, tile, last - first + 1,
+                                                          wi - first);
             if (tid == 0 && fin) atomicAdd(a.sync + kLine * u, 1);  // h-ready count of unit u
         }
-        if (want_status && cur < 0) resolve(0, true, e, g);  // an empty share still reports the status
+        if (want_status && cur < 0) resolve(0, true, e, g, sh);  // an empty share still reports the status
     } else {
         const int item = (int)blockIdx.x - a.g1;
         const int u = item / a.T2, t = item - u * a.T2;
@@ -593,15 +616,17 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
         int32_t* dcnt = hcnt + 1;                // this unit's finished down items
         int32_t* ocnt = a.sync + kLine * (MOE_MAX_SLOTS + t);  // arrivals on this down tile
         int e, g;
-        resolve(u, false, e, g);
+        bool sh;
+        resolve(u, false, e, g, sh);
         // ================ down: O for RT2 rows of d ================
         if (g > 0) {
             const uint32_t mat = (uint32_t)a.d * a.d_ff * F::kEsize;
-            const auto rd = rsrc(a.wd + (size_t)e * mat, mat);
-            const uint32_t hbytes = (uint32_t)nm * a.d_ff * F::kEsize;
+            const auto rd = rsrc((SH && sh ? a.wds : a.wd) + (size_t)e * mat, mat);
+            const int nslot = SH ? a.nslot : nm;
+            const uint32_t hbytes = (uint32_t)nslot * a.d_ff * F::kEsize;
             const auto rh = rsrc(a.h, hbytes);
             const auto rl = rsrc(a.h + (BF16 ? hbytes : 0), hbytes);
-            const auto ro = rsrc(a.O, (uint32_t)nm * a.d * 4);
+            const auto ro = rsrc(a.O, (uint32_t)nslot * a.d * 4);
             const int S = (a.d_ff + F::kStep - 1) / F::kStep;
             const int s0 = wave * S / kWaves;
             const Steps<BF16, KF> st{s0, (wave + 1) * S / kWaves - s0, a.d_ff, q};
@@ -787,12 +812,13 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
         }
         __syncthreads();  // O loads (sc1) below are issued after the last arrival was seen
         if (s_last) {
-            // y_t = sum_j w_tj O_tj for 4 rows per thread, slots in increasing j;
-            // the O loads (sc1) of up to kCJ slots are in flight together
+            // y_t = sum_j w_tj O_tj + sum_s O_(shared s, t) for 4 rows per thread,
+            // slots in increasing j, then shared experts in increasing s; the O loads
+            // (sc1) of up to kCJ slots are in flight together
             constexpr int kCJ = 8;
             const int i0 = t * RT2;
             const int q4 = min(RT2, a.d - i0) / 4;  // d % 8 == 0
-            const auto rO = rsrc(a.O, (uint32_t)nm * a.d * 4);
+            const auto rO = rsrc(a.O, (uint32_t)(SH ? a.nslot : nm) * a.d * 4);
             for (int o = tid; o < a.n * q4; o += kThreads) {
                 const int tok = o / q4, i = i0 + 4 * (o - tok * q4);
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -813,6 +839,19 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
                         if (ok[jj])
 #pragma unroll
                             for (int r = 0; r < 4; ++r) acc[r] = fmaf(wv[jj], __uint_as_float(ov[jj][r]), acc[r]);
+                }
+                for (int s0 = 0; SH && s0 < a.n_shared; s0 += kCJ) {
+                    u32x4 ov[kCJ];
+#pragma unroll
+                    for (int ss = 0; ss < kCJ; ++ss) {
+                        const int sl = nm + (s0 + ss) * a.n + tok;
+                        ov[ss] = bload_sc1(rO, s0 + ss < a.n_shared ? ((uint32_t)sl * a.d + i) * 4 : kOOB);
+                    }
+#pragma unroll
+                    for (int ss = 0; ss < kCJ; ++ss)
+                        if (s0 + ss < a.n_shared)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) acc[r] += __uint_as_float(ov[ss][r]);
                 }
                 f32x4* yp = reinterpret_cast<f32x4*>(a.y + (size_t)tok * a.d + i);
                 *yp = a.accumulate ? *yp + acc : acc;
@@ -946,11 +985,17 @@ int check_desc(const moe_layer_desc* d, int32_t n) {
     // one expert matrix must be addressable by a 31-bit buffer offset
     if ((int64_t)d->d_model * d->d_ff * es > (1ll << 31) - 4096) return MOE_E_INVAL;
     if ((d->d_model + kTile - 1) / kTile > kMaxDownTiles) return MOE_E_INVAL;  // d_model <= 16384
+    // shared experts: one counter line per unit, and h and O rows addressable by a
+    // 31-bit buffer offset
+    if (d->n_shared < 0 || d->n_shared > MOE_MAX_SHARED) return MOE_E_INVAL;
+    if ((int64_t)n * d->m + d->n_shared > MOE_MAX_SLOTS) return MOE_E_INVAL;
+    const int64_t nslot = (int64_t)n * d->m + (int64_t)d->n_shared * n;
+    if (nslot * d->d_ff * 4 > (1ll << 31) - 4096 || nslot * d->d_model * 4 > (1ll << 31) - 4096) return MOE_E_INVAL;
     return MOE_OK;
 }
 
 struct Plan {
-    int units, T1, T2, nt, rb;
+    int units, units_r, nslot, T1, T2, nt, rb;
     int g1, S1;  // gate/up work groups, K steps per gate/up tile
     size_t part_off;
     bool dpf;    // down items in register mode
@@ -960,12 +1005,21 @@ struct Plan {
 };
 
 constexpr int kHsBudget = 24 * 1024;  // LDS bytes for staged h (down items in register mode)
+// per-slot passes with shared experts: LDS for the shared experts' h chunks
+constexpr int kHsBudgetShared = 12 * 1024;
 
 Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     Plan p;
     const int nm = n * d->m;
-    p.units = kind == MOE_KIND_SLOT ? nm : (nm < d->N ? nm : d->N);
-    p.nt = kind == MOE_KIND_SLOT ? 1 : (n <= 16 ? 1 : (n <= 32 ? 2 : 4));
+    // routed units, then one unit per shared expert (all n tokens)
+    p.units_r = kind == MOE_KIND_SLOT ? nm : (nm < d->N ? nm : d->N);
+    p.units = p.units_r + d->n_shared;
+    p.nslot = nm + d->n_shared * n;
+    // token columns per MFMA pass: a group of up to 16 tokens is one column tile;
+    // larger groups (dedup, or a shared expert's n tokens) take 2 or 4 so that each
+    // expert is still read once
+    const bool wide = kind == MOE_KIND_DEDUP || d->n_shared > 0;
+    p.nt = (!wide || n <= 16) ? 1 : (n <= 32 ? 2 : 4);
     p.rb = p.nt == 4 ? 1 : 2;  // rows per item = 16 * rb; row blocks x token tiles <= 4
     p.T1 = (d->d_ff + kTile * p.rb - 1) / (kTile * p.rb);
     // register mode when a wave's share of the down contraction fits kPF steps
@@ -973,53 +1027,83 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     const int es = bf ? 2 : 4, step = 64 / es;
     const int s2 = (d->d_ff + step - 1) / step;
     const int per_tok = (d->d_ff * es + 16) * (bf ? 2 : 1);  // staged bytes per token
-    const int gmax = kind == MOE_KIND_SLOT ? 1 : n;  // group size is at most n (valid ids)
+    const int gmax = kind == MOE_KIND_SLOT ? 1 : n;  // routed group size is at most n (valid ids)
     // (and only when one LDS chunk of at most 16 tokens, one MFMA column tile,
     // holds a whole group: several chunks would serialise their h loads and O
-    // stores)
-    p.dpf = (s2 + kWaves - 1) / kWaves <= kPF && gmax <= 16 && (int64_t)per_tok * gmax <= kHsBudget;
-    p.gl = p.dpf ? gmax : 0;
+    // stores).  A per-slot pass with shared experts stages their n tokens in
+    // chunks of what kHsBudgetShared holds.
+    const bool steps_fit = (s2 + kWaves - 1) / kWaves <= kPF;
+    if (kind == MOE_KIND_SLOT && d->n_shared > 0) {
+        const int cap = (int)std::max<int64_t>(1, kHsBudgetShared / per_tok);
+        p.dpf = steps_fit && (int64_t)per_tok <= kHsBudget;
+        p.gl = p.dpf ? std::min(n, std::min(cap, 16)) : 0;
+    } else {
+        p.dpf = steps_fit && gmax <= 16 && (int64_t)per_tok * gmax <= kHsBudget;
+        p.gl = p.dpf ? gmax : 0;
+    }
     p.lds = p.dpf ? (size_t)p.gl * per_tok : 0;
     const int rb2 = p.dpf ? 1 : p.rb;
     p.T2 = (d->d_model + kTile * rb2 - 1) / (kTile * rb2);
     // Gate/up work is cut into kCUs equal shares when there are between half and
     // twice as many tiles as compute units: then no compute unit holds two tiles
-    // while another holds one.  Each share is at least half a tile, so a tile is
+    // while another holds one.  With fewer tiles than half the compute units (a
+    // pass of one or two experts), every tile is cut in two, so twice as many
+    // compute units stream (a compute unit's own stream is bounded by the loads
+    // it keeps in flight).  Each share is at least half a tile, so a tile is
     // shared by at most kMaxContrib work groups.  Otherwise one work group per
     // tile (with more tiles, cutting them measured slower than the imbalance).
     p.S1 = (d->d_model + step - 1) / step;
     const int64_t tiles = (int64_t)p.units * p.T1;
-    const int64_t part_bytes = (int64_t)kMaxContrib * nm * d->d_ff * 8;
-    const bool split = tiles * 2 >= kCUs && tiles < 2 * kCUs && part_bytes <= (64ll << 20);
-    p.g1 = split ? kCUs : (int)tiles;
+    const int64_t part_bytes = (int64_t)kMaxContrib * p.nslot * d->d_ff * 8;
+    const bool few = tiles * 2 < kCUs && p.S1 >= 2;
+    const bool split = ((tiles * 2 >= kCUs && tiles < 2 * kCUs) || few) && part_bytes <= (64ll << 20);
+    p.g1 = !split ? (int)tiles : (few ? (int)(2 * tiles) : kCUs);
     p.sync_off = 0;
     p.h_off = (size_t)kSyncWords * 4;
-    p.o_off = p.h_off + align_up((size_t)nm * d->d_ff * 4);
-    p.part_off = p.o_off + align_up((size_t)nm * d->d_model * 4);
+    p.o_off = p.h_off + align_up((size_t)p.nslot * d->d_ff * 4);
+    p.part_off = p.o_off + align_up((size_t)p.nslot * d->d_model * 4);
     p.total = p.part_off + (split ? align_up((size_t)part_bytes) : 0);
     return p;
 }
 
-template <bool BF16, int MODE, int NT, int RB, bool PK>
+template <bool BF16, int MODE, int NT, int RB, bool PK, bool SH>
 void launch_pk(const Args& args, const Plan& p, int grid, hipStream_t st) {
     constexpr int step = Fmt<BF16>::kStep;
     const bool kf = args.d % step == 0 && args.d_ff % step == 0;
     if (kf && p.dpf)
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, true, PK>), dim3(grid), dim3(kThreads), p.lds, st,
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, true, PK, SH>), dim3(grid), dim3(kThreads), p.lds, st,
                            args);
     else if (kf)
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, false, PK>), dim3(grid), dim3(kThreads), 0, st, args);
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, false, PK, SH>), dim3(grid), dim3(kThreads), 0, st,
+                           args);
     else if (p.dpf)
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, true, PK>), dim3(grid), dim3(kThreads), p.lds, st,
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, true, PK, SH>), dim3(grid), dim3(kThreads), p.lds, st,
                            args);
     else
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, false, PK>), dim3(grid), dim3(kThreads), 0, st, args);
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, false, PK, SH>), dim3(grid), dim3(kThreads), 0, st,
+                           args);
 }
 
-template <bool BF16, int MODE, int NT, int RB>
-void launch(const Args& args, const Plan& p, int grid, hipStream_t st, bool packed) {
-    if (packed) launch_pk<BF16, MODE, NT, RB, true>(args, p, grid, st);
-    else launch_pk<BF16, MODE, NT, RB, false>(args, p, grid, st);
+// Kernel variant for the plan.  Shared experts (SH) are a variant of their own, so
+// that passes without them carry none of their registers; a per-slot pass without
+// them always takes one token column tile.
+template <bool BF16, int MODE, bool SH>
+void launch_nt(const Args& args, const Plan& p, int grid, hipStream_t st, bool pk) {
+    if constexpr (MODE == kPerSlot && !SH) {
+        if (pk) launch_pk<BF16, MODE, 1, 2, true, SH>(args, p, grid, st);
+        else launch_pk<BF16, MODE, 1, 2, false, SH>(args, p, grid, st);
+    } else {
+        if (p.nt == 1) {
+            if (pk) launch_pk<BF16, MODE, 1, 2, true, SH>(args, p, grid, st);
+            else launch_pk<BF16, MODE, 1, 2, false, SH>(args, p, grid, st);
+        } else if (p.nt == 2) {
+            if (pk) launch_pk<BF16, MODE, 2, 2, true, SH>(args, p, grid, st);
+            else launch_pk<BF16, MODE, 2, 2, false, SH>(args, p, grid, st);
+        } else {
+            if (pk) launch_pk<BF16, MODE, 4, 1, true, SH>(args, p, grid, st);
+            else launch_pk<BF16, MODE, 4, 1, false, SH>(args, p, grid, st);
+        }
+    }
 }
 
 template <int MODE>
@@ -1030,6 +1114,9 @@ int run_expert(const moe_layer_desc* d, const moe_layer_weights* W, const void* 
     if (rc != MOE_OK) return rc;
     if (!W || !W->w_gate || !W->w_up || !W->w_down || !x || !ids || !w || !y || !ws) return MOE_E_INVAL;
     if (!aligned16(W->w_gate) || !aligned16(W->w_up) || !aligned16(W->w_down) || !aligned16(x) || !aligned16(y))
+        return MOE_E_INVAL;
+    if (d->n_shared > 0 && (!W->w_gate_shared || !W->w_up_shared || !W->w_down_shared ||
+                            !aligned16(W->w_gate_shared) || !aligned16(W->w_up_shared) || !aligned16(W->w_down_shared)))
         return MOE_E_INVAL;
     if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return MOE_E_INVAL;
     const int kind = MODE == kPerSlot ? MOE_KIND_SLOT : MOE_KIND_DEDUP;
@@ -1046,6 +1133,9 @@ int run_expert(const moe_layer_desc* d, const moe_layer_weights* W, const void* 
     args.wg = reinterpret_cast<const char*>(W->w_gate);
     args.wu = reinterpret_cast<const char*>(W->w_up);
     args.wd = reinterpret_cast<const char*>(W->w_down);
+    args.wgs = reinterpret_cast<const char*>(d->n_shared > 0 ? W->w_gate_shared : nullptr);
+    args.wus = reinterpret_cast<const char*>(d->n_shared > 0 ? W->w_up_shared : nullptr);
+    args.wds = reinterpret_cast<const char*>(d->n_shared > 0 ? W->w_down_shared : nullptr);
     args.x = reinterpret_cast<const char*>(x);
     args.ids = ids;
     args.w = w;
@@ -1060,6 +1150,9 @@ int run_expert(const moe_layer_desc* d, const moe_layer_weights* W, const void* 
     args.d = d->d_model;
     args.d_ff = d->d_ff;
     args.units = p.units;
+    args.units_r = p.units_r;
+    args.n_shared = d->n_shared;
+    args.nslot = p.nslot;
     args.T1 = p.T1;
     args.T2 = p.T2;
     args.accumulate = (d->flags & MOE_FLAG_ACCUMULATE) ? 1 : 0;
@@ -1072,14 +1165,13 @@ int run_expert(const moe_layer_desc* d, const moe_layer_weights* W, const void* 
     if (events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(events[0]), st);
     const bool bf = d->dtype == MOE_BF16;
     const bool pk = (d->flags & MOE_FLAG_WDOWN_PACKED) != 0;
+    const bool sh = d->n_shared > 0;
     if (bf) {
-        if (p.nt == 1) launch<true, MODE, 1, 2>(args, p, grid, st, pk);
-        else if (p.nt == 2) launch<true, MODE, 2, 2>(args, p, grid, st, pk);
-        else launch<true, MODE, 4, 1>(args, p, grid, st, pk);
+        if (sh) launch_nt<true, MODE, true>(args, p, grid, st, pk);
+        else launch_nt<true, MODE, false>(args, p, grid, st, pk);
     } else {
-        if (p.nt == 1) launch<false, MODE, 1, 2>(args, p, grid, st, pk);
-        else if (p.nt == 2) launch<false, MODE, 2, 2>(args, p, grid, st, pk);
-        else launch<false, MODE, 4, 1>(args, p, grid, st, pk);
+        if (sh) launch_nt<false, MODE, true>(args, p, grid, st, pk);
+        else launch_nt<false, MODE, false>(args, p, grid, st, pk);
     }
     if (events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(events[1]), st);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
@@ -1115,6 +1207,7 @@ int moe_pack_w_down(const moe_layer_desc* desc, const void* w_down, void* w_down
     if (!desc) return MOE_E_INVAL;
     moe_layer_desc dd = *desc;
     dd.flags = 0;
+    dd.n_shared = 0;
     const int rc = check_desc(&dd, 1);
     if (rc != MOE_OK) return rc;
     if (!w_down || !w_down_packed || !aligned16(w_down) || !aligned16(w_down_packed)) return MOE_E_INVAL;

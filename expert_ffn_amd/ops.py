@@ -46,34 +46,58 @@ def _check_dev(name, t, dtype=None, shape=None):
 class Layer:
     """Device weights of one MoE layer: W_gate, W_up [N][d_ff][d], W_down [N][d][d_ff],
     or, with ``packed``, W_down in the layout of ``moe_pack_w_down``,
-    [N][d_ff/8][d][8] (see ``Layer.packed_copy``)."""
+    [N][d_ff/8][d][8] (see ``Layer.packed_copy``).  ``shared``: the always-on
+    experts' (W_gate, W_up, W_down), [n_shared][...] in the same layouts, computed in
+    the same call as the routed experts."""
 
-    def __init__(self, w_gate, w_up, w_down, m, packed=False):
+    def __init__(self, w_gate, w_up, w_down, m, packed=False, shared=None):
         N, d_ff, d = w_gate.shape
         _check_dev("w_gate", w_gate)
         _check_dev("w_up", w_up, w_gate.dtype, (N, d_ff, d))
-        if packed:
-            _check_dev("w_down", w_down, w_gate.dtype, (N, d_ff // 8, d, 8))
-        else:
-            _check_dev("w_down", w_down, w_gate.dtype, (N, d, d_ff))
-        self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
+        self.packed = bool(packed)
         self.N, self.m, self.d, self.d_ff = N, int(m), d, d_ff
         self.dtype = w_gate.dtype
-        self.packed = bool(packed)
-        self._weights = _abi.LayerWeights(w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr())
+        _check_dev("w_down", w_down, w_gate.dtype, self._down_shape(N))
+        self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
+        self.shared = None
+        self.n_shared = 0
+        ptrs = [0, 0, 0]
+        if shared is not None:
+            sg, su, sd = shared
+            S = sg.shape[0]
+            if not 1 <= S <= _abi.MOE_MAX_SHARED:
+                raise ValueError("n_shared must be in 1..%d, got %d" % (_abi.MOE_MAX_SHARED, S))
+            _check_dev("w_gate_shared", sg, self.dtype, (S, d_ff, d))
+            _check_dev("w_up_shared", su, self.dtype, (S, d_ff, d))
+            _check_dev("w_down_shared", sd, self.dtype, self._down_shape(S))
+            self.shared = (sg, su, sd)
+            self.n_shared = S
+            ptrs = [sg.data_ptr(), su.data_ptr(), sd.data_ptr()]
+        self._weights = _abi.LayerWeights(w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr(), *ptrs)
+
+    def _down_shape(self, E):
+        return (E, self.d_ff // 8, self.d, 8) if self.packed else (E, self.d, self.d_ff)
 
     def desc(self, accumulate=False):
         flags = (_abi.MOE_FLAG_ACCUMULATE if accumulate else 0) | (_abi.MOE_FLAG_WDOWN_PACKED if self.packed else 0)
-        return _abi.LayerDesc(self.N, self.m, self.d, self.d_ff, _dtype_code(self.w_gate), flags)
+        return _abi.LayerDesc(self.N, self.m, self.d, self.d_ff, _dtype_code(self.w_gate), flags, self.n_shared)
 
     def packed_copy(self, stream=None):
-        """The same layer with W_down packed by ``moe_pack_w_down`` (a new device tensor;
-        W_gate and W_up shared)."""
+        """The same layer with W_down (and the shared experts' W_down) packed by
+        ``moe_pack_w_down`` (new device tensors; W_gate and W_up shared)."""
         if self.packed:
             return self
-        dst = torch.empty((self.N, self.d_ff // 8, self.d, 8), dtype=self.dtype, device=self.w_down.device)
-        pack_w_down(self, self.w_down, dst, stream=stream)
-        return Layer(self.w_gate, self.w_up, dst, self.m, packed=True)
+
+        def pk(wd):
+            E = wd.shape[0]
+            dst = torch.empty((E, self.d_ff // 8, self.d, 8), dtype=self.dtype, device=wd.device)
+            return pack_w_down(self, wd, dst, stream=stream)
+        sh = None if self.shared is None else (self.shared[0], self.shared[1], pk(self.shared[2]))
+        return Layer(self.w_gate, self.w_up, pk(self.w_down), self.m, packed=True, shared=sh)
+
+    def without_shared(self):
+        """The routed experts alone (same tensors)."""
+        return Layer(self.w_gate, self.w_up, self.w_down, self.m, packed=self.packed)
 
     @property
     def expert_bytes(self):
@@ -88,10 +112,12 @@ class Layer:
 
 
 def pack_w_down(layer, w_down, out, stream=None):
-    """Copy W_down [N][d][d_ff] into the packed layout [N][d_ff/8][d][8] (one launch)."""
-    _check_dev("w_down", w_down, layer.dtype, (layer.N, layer.d, layer.d_ff))
-    _check_dev("out", out, layer.dtype, (layer.N, layer.d_ff // 8, layer.d, 8))
-    desc = _abi.LayerDesc(layer.N, layer.m, layer.d, layer.d_ff, _dtype_code(layer.w_gate), 0)
+    """Copy W_down [E][d][d_ff] (E experts: the layer's N, or its shared experts) into
+    the packed layout [E][d_ff/8][d][8] (one launch)."""
+    E = w_down.shape[0]
+    _check_dev("w_down", w_down, layer.dtype, (E, layer.d, layer.d_ff))
+    _check_dev("out", out, layer.dtype, (E, layer.d_ff // 8, layer.d, 8))
+    desc = _abi.LayerDesc(E, 1, layer.d, layer.d_ff, _dtype_code(layer.w_gate), 0, 0)
     check("moe_pack_w_down", lib().moe_pack_w_down(ctypes.byref(desc), _vp(w_down), _vp(out), _stream(stream)))
     return out
 

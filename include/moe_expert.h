@@ -61,26 +61,35 @@ enum { MOE_KIND_SLOT = 0, MOE_KIND_DEDUP = 1 };
 #define MOE_MAX_SLOTS 256     /* n * m */
 #define MOE_MAX_TOKENS 64     /* n */
 #define MOE_MAX_EXPERTS 1024  /* N */
+#define MOE_MAX_SHARED 16     /* n_shared */
 #define MOE_FLAG_ACCUMULATE 1u /* y += result (else y = result) */
 /* w_down is in the packed layout of moe_pack_w_down (else [N][d_model][d_ff]) */
 #define MOE_FLAG_WDOWN_PACKED 2u
 
-/* One MoE layer.  1 <= m <= N (m == N is allowed so that always-on shared
- * experts can run as a layer whose every token selects all of them). */
+/* One MoE layer.  1 <= m <= N (m == N is allowed, so that always-on experts can
+ * also run as a layer of their own whose every token selects all of them). */
 typedef struct {
-    int32_t N;       /* experts in the layer */
-    int32_t m;       /* experts selected per token */
-    int32_t d_model; /* d: token width; multiple of 8 */
-    int32_t d_ff;    /* expert hidden width; multiple of 8 */
-    int32_t dtype;   /* moe_dtype of the weights and of x */
-    uint32_t flags;  /* MOE_FLAG_* */
+    int32_t N;        /* routed experts in the layer */
+    int32_t m;        /* experts selected per token */
+    int32_t d_model;  /* d: token width; multiple of 8 */
+    int32_t d_ff;     /* expert hidden width; multiple of 8 */
+    int32_t dtype;    /* moe_dtype of the weights and of x */
+    uint32_t flags;   /* MOE_FLAG_* */
+    int32_t n_shared; /* always-on (shared) experts computed in the same call,
+                         0 .. MOE_MAX_SHARED; 0 = none.  Same d_model, d_ff, dtype
+                         and W_down layout as the routed experts. */
 } moe_layer_desc;
 
-/* Device pointers, caller-owned, 16-byte aligned, layouts as above. */
+/* Device pointers, caller-owned, 16-byte aligned, layouts as above.  The shared
+ * experts' tensors hold n_shared experts ([n_shared][d_ff][d_model] and so on) and
+ * are read only when desc->n_shared > 0 (else they may be NULL). */
 typedef struct {
     const void* w_gate;
     const void* w_up;
     const void* w_down;
+    const void* w_gate_shared;
+    const void* w_up_shared;
+    const void* w_down_shared;
 } moe_layer_weights;
 
 /*
@@ -106,11 +115,12 @@ int moe_route_group(const int32_t* ids, int32_t n, int32_t m, int32_t N, int32_t
 
 /* Workspace bytes that moe_expert_perslot (kind MOE_KIND_SLOT) or
  * moe_expert_dedup (MOE_KIND_DEDUP) needs for passes of up to n tokens; 0 on
- * invalid arguments.  For a pass of k tokens the workspace holds 224 KB of
- * synchronisation counters (one per 128-byte line), the per-slot hidden
- * activations and expert outputs (k*m*(d_ff + d_model)*4 bytes) and, when the
- * pass's gate/up work is 128 to 511 row tiles, the partial sums of tiles that
- * work groups share (3*k*m*d_ff*8 bytes), each piece aligned to 256 bytes.  The
+ * invalid arguments.  For a pass of k tokens with S = k*m + n_shared*k slots (the
+ * routed slots, then one per token and shared expert) the workspace holds 224 KB
+ * of synchronisation counters (one per 128-byte line), the slots' hidden
+ * activations and expert outputs (S*(d_ff + d_model)*4 bytes) and, when the
+ * pass's gate/up work is fewer than 511 row tiles, the partial sums of tiles that
+ * work groups share (3*S*d_ff*8 bytes), each piece aligned to 256 bytes.  The
  * size returned is the largest over k = 1..n, so a workspace sized for n serves
  * every smaller n of the same layer.  d_model is limited to 16384. */
 size_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t n, int32_t kind);
@@ -119,6 +129,11 @@ size_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t n, int32_t kind);
  * moe_expert_perslot -- the expert operation by the per-slot kernel: every slot
  * reads its expert's W_gate, W_up and W_down rows once (n*m expert reads per
  * pass, paper Section 1 "Bytes": E_slot(n) = n m w).  One kernel launch.
+ * With desc->n_shared > 0 the same launch also computes the always-on experts,
+ * each read once per pass against all n tokens with weight 1 (the D(n) bytes of
+ * paper Eq. 5, outside E_p, in both kernels), and adds them to each token's y
+ * after its routed slots, in increasing shared-expert index.
+ * Limits: n*m + n_shared <= MOE_MAX_SLOTS.
  *   x    device [n][d_model]  (dtype of desc)
  *   ids  device [n][m]        ids outside [0, N) are skipped (their slot adds 0)
  *   w    device [n][m] fp32   routing weights
@@ -190,7 +205,8 @@ int moe_expert_dedup_ev(const moe_layer_desc* desc, const moe_layer_weights* wei
  * ids (host [n][m]) are given (paper Section 1 "Bytes" and Section 3.1): with
  * w = 3 d_model d_ff sizeof(W),
  *     MOE_KIND_SLOT:  n m w           MOE_KIND_DEDUP:  X(n) w   (byte factor f = 1)
- * x, y, ids and routing-weight bytes are not counted.  Host only, synchronous.
+ * x, y, ids and routing-weight bytes are not counted, nor are the always-on experts
+ * of desc->n_shared (the D(n) term of Eq. 5).  Host only, synchronous.
  * Returns the byte count, or -MOE_E_* (negative) for invalid arguments or ids.
  */
 int64_t bytes_requested(int32_t kind, const moe_layer_desc* desc, const int32_t* ids_host,

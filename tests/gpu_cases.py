@@ -22,33 +22,46 @@ def say(*a):
 
 
 class DeviceLayer:
-    """Host weights (for the oracle) and their device copy (for the kernels)."""
+    """Host weights (for the oracle) and their device copy (for the kernels).  With
+    shared experts: ``shared_dev`` holds them as a layer of their own (m = N =
+    n_shared, run as a second call) and ``fused`` the routed and shared experts as
+    one layer (one call)."""
 
     def __init__(self, spec, seed, layer=0, with_shared=False, host=None, packed=False):
         self.spec = spec
         self.host = host if host is not None else synth.layer_weights(spec, seed, layer)
         self.dev = efa.Layer(*(to_torch(a) for a in self.host), m=spec.m)
-        if packed:  # W_down in the packed layout (moe_pack_w_down); the plain copy is dropped
-            self.dev = self.dev.packed_copy()
-            torch.cuda.synchronize()
         self.shared_host = None
         self.shared_dev = None
+        self.fused = None
         if with_shared and spec.n_shared:
             self.shared_host = synth.layer_weights(spec, seed, layer, shared=True)
             self.shared_dev = efa.Layer(*(to_torch(a) for a in self.shared_host), m=spec.n_shared)
+            sd = self.shared_dev
+            self.fused = efa.Layer(self.dev.w_gate, self.dev.w_up, self.dev.w_down, m=spec.m,
+                                   shared=(sd.w_gate, sd.w_up, sd.w_down))
+        if packed:  # W_down in the packed layout (moe_pack_w_down); the plain copies are dropped
+            self.dev = self.dev.packed_copy()
+            if self.fused is not None:
+                self.fused = self.fused.packed_copy()
+                self.shared_dev = self.shared_dev.packed_copy()
+            torch.cuda.synchronize()
 
     def run(self, x_host, ids_host, w_host, shared=False, stream=None):
-        """Returns (y_perslot, y_dedup, info_dedup) on the host; info = (U, ids status, sync status)."""
+        """Returns (y_perslot, y_dedup, info_dedup) on the host; info = (U, ids status, sync status).
+        shared: False (routed experts only), "separate" (a second, accumulating call on
+        the shared experts' own layer) or "fused" (one call with the shared experts)."""
         x = to_torch(x_host)
         ids = torch.from_numpy(np.ascontiguousarray(ids_host, np.int32)).cuda()
         w = torch.from_numpy(np.ascontiguousarray(w_host, np.float32)).cuda()
         n = x.shape[0]
-        ws = self.dev.workspace(n)
+        layer = self.fused if shared == "fused" else self.dev
+        ws = layer.workspace(n)
         info_s = torch.full((3,), 99, dtype=torch.int32, device="cuda")
         info_d = torch.full((3,), 99, dtype=torch.int32, device="cuda")
-        ys = efa.expert_perslot(self.dev, x, ids, w, ws=ws, info=info_s, stream=stream)
-        yd = efa.expert_dedup(self.dev, x, ids, w, ws=ws, info=info_d, stream=stream)
-        if shared:
+        ys = efa.expert_perslot(layer, x, ids, w, ws=ws, info=info_s, stream=stream)
+        yd = efa.expert_dedup(layer, x, ids, w, ws=ws, info=info_d, stream=stream)
+        if shared == "separate":
             E = self.spec.n_shared
             sids = torch.arange(E, dtype=torch.int32, device="cuda").repeat(n, 1).contiguous()
             sw = torch.ones(n, E, dtype=torch.float32, device="cuda")

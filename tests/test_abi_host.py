@@ -36,9 +36,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def _desc(**kw):
-    d = dict(N=8, m=2, d_model=64, d_ff=128, dtype=_abi.MOE_F32, flags=0)
+    d = dict(N=8, m=2, d_model=64, d_ff=128, dtype=_abi.MOE_F32, flags=0, n_shared=0)
     d.update(kw)
-    return _abi.LayerDesc(d["N"], d["m"], d["d_model"], d["d_ff"], d["dtype"], d["flags"])
+    return _abi.LayerDesc(d["N"], d["m"], d["d_model"], d["d_ff"], d["dtype"], d["flags"], d["n_shared"])
 
 
 def test_host_validation_rejects_before_launch():
@@ -72,7 +72,10 @@ def test_host_validation_rejects_before_launch():
     assert L.moe_expert_perslot(ctypes.byref(d), ctypes.byref(Wm), fake, fake, fake, 4, fake, None, fake, 1 << 30,
                                 None) == _abi.MOE_E_INVAL
     need = L.moe_workspace_bytes(ctypes.byref(d), 4, 0)
-    assert need == 229376 + 4 * 2 * 128 * 4 + 4 * 2 * 64 * 4  # sync area + h + O (256-aligned pieces)
+    # sync area + h + O + partial sums of split tiles (256-aligned pieces): fewer gate/up
+    # tiles than half the compute units are each cut in two, so the workspace holds
+    # 3 contributors x n*m x d_ff x (gate, up) fp32
+    assert need == 229376 + 4 * 2 * 128 * 4 + 4 * 2 * 64 * 4 + 3 * 4 * 2 * 128 * 8
     assert L.moe_workspace_bytes(ctypes.byref(d), 4, 1) == need
     # 128 .. 511 gate/up tiles: the workspace also holds partial sums of split
     # tiles, 3 contributors x n*m x d_ff x (gate, up) fp32 (per-slot: 44 tiles per
@@ -103,6 +106,20 @@ def test_host_validation_rejects_before_launch():
                                    None, ev, 3) == _abi.MOE_E_INVAL
     assert L.moe_expert_dedup_ev(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 4, fake, None, fake, need,
                                  None, None, 2) == _abi.MOE_E_INVAL
+    # shared experts: count limit, units limit (n*m + n_shared <= 256), null or
+    # misaligned shared pointers; the workspace grows by n_shared*n slots
+    Ws = _abi.LayerWeights(0x1000, 0x1000, 0x1000, 0x2000, 0x2000, 0x2000)
+    for desc, Wx, n in ((_desc(n_shared=17), Ws, 4), (_desc(n_shared=-1), Ws, 4),
+                        (_desc(N=64, m=4, n_shared=5), Ws, 63), (_desc(n_shared=2), W, 4),
+                        (_desc(n_shared=2), _abi.LayerWeights(0x1000, 0x1000, 0x1000, 0x2000, 0x2008, 0x2000), 4)):
+        for fn in (L.moe_expert_perslot, L.moe_expert_dedup):
+            assert fn(ctypes.byref(desc), ctypes.byref(Wx), fake, fake, fake, n, fake, None, fake, 1 << 30,
+                      None) == _abi.MOE_E_INVAL
+    assert L.moe_workspace_bytes(ctypes.byref(_desc(N=64, m=4, n_shared=4)), 63, 0) > 0
+    assert L.moe_workspace_bytes(ctypes.byref(_desc(N=64, m=4, n_shared=5)), 63, 0) == 0
+    ds = _desc(n_shared=2)
+    S = 4 * 2 + 2 * 4
+    assert L.moe_workspace_bytes(ctypes.byref(ds), 4, 0) == 229376 + S * 128 * 4 + S * 64 * 4 + 3 * S * 128 * 8
     assert L.moe_kernels_per_call(0) == 1 and L.moe_kernels_per_call(1) == 1
     assert L.moe_kernels_per_call(5) == _abi.MOE_E_INVAL
     # grouping limits

@@ -66,7 +66,7 @@ def _agree(ys, yd, what):
 def _compare(dl, x, ids, w, what, shared=False, tokens=None):
     ys, yd, info = dl.run(x, ids, w, shared=shared)
     assert info[0] == oracle.union_count(ids, dl.spec.N) and info[1] == 0
-    ref = dl.oracle_y(x, ids, w, shared=shared, tokens=tokens)
+    ref = dl.oracle_y(x, ids, w, shared=bool(shared), tokens=tokens)
     sel = slice(None) if tokens is None else tokens
     r1 = assert_close(ys[sel], ref, what + " perslot")
     r2 = assert_close(yd[sel], ref, what + " dedup")
@@ -214,8 +214,50 @@ def test_dsv2lite_windows(dsv2, dsv2p, kind, packed):
         st = int(starts[n - 1])
         ids, w = routing.window(tr, st, n)
         x = synth.pass_x(spec, 2026, 0, 1000 + n, n)
-        say("dsv2lite", kind, "n", n, "start", st)
-        _compare(dsv2, x, ids, w, "dsv2lite %s n=%d" % (kind, n), shared=(n in (1, 5)))
+        sh = "separate" if n in (1, 5) else ("fused" if n in (2, 3, 8) else False)
+        say("dsv2lite", kind, "n", n, "start", st, "shared", sh)
+        _compare(dsv2, x, ids, w, "dsv2lite %s n=%d" % (kind, n), shared=sh)
+
+
+@pytest.mark.parametrize("base,n_shared,d,d_ff", [("tiny", 1, 64, 128), ("tiny", 3, 72, 40),
+                                                   ("dsv2lite", 2, 96, 160), ("dsv2lite", 1, 256, 352)])
+@pytest.mark.parametrize("packed", [False, True])
+def test_shared_experts_in_the_same_call(base, n_shared, d, d_ff, packed):
+    """Always-on experts computed in the same launch as the routed ones (each read once
+    per pass against all n tokens, weight 1), for both kernels, against the oracle's
+    shared-expert sum; n = 17 and 20 take two token columns per MFMA pass."""
+    spec = synth.layer_spec(base, N=12, m=3, d=d, d_ff=d_ff, n_shared=n_shared)
+    dl = DeviceLayer(spec, 31, with_shared=True, packed=packed)
+    tr = routing.make_trace(spec, "correlated", 64, seed=31, p=0.5)
+    for n in (1, 2, 5, 8, 17, 20):
+        ids, w = routing.window(tr, 3, n)
+        x = synth.pass_x(spec, 31, 0, n, n)
+        say("shared", base, n_shared, d, d_ff, "packed", packed, "n", n)
+        _compare(dl, x, ids, w, "shared %s S=%d n=%d" % (base, n_shared, n), shared="fused")
+
+
+def test_shared_experts_accumulate_and_most_units():
+    """With MOE_FLAG_ACCUMULATE the fused call adds to y; a pass at the unit limit
+    (n*m + n_shared = 256) still matches the oracle."""
+    spec = synth.layer_spec("dsv2lite", N=64, m=4, d=128, d_ff=96, n_shared=4)
+    dl = DeviceLayer(spec, 5, with_shared=True, packed=True)
+    tr = routing.make_trace(spec, "uniform", 128, seed=5)
+    n = 63  # 63*4 + 4 = 256 units
+    ids, w = routing.window(tr, 0, n)
+    x_h = synth.pass_x(spec, 5, 0, 0, n)
+    say("shared at the unit limit, n", n)
+    _compare(dl, x_h, ids, w, "shared unit limit", shared="fused")
+    x = to_torch(x_h)
+    idd = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
+    wd = torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()
+    y0 = torch.randn(n, spec.d, dtype=torch.float32, device="cuda")
+    ws = dl.fused.workspace(n)
+    for fn in (efa.expert_perslot, efa.expert_dedup):
+        y = y0.clone()
+        fn(dl.fused, x, idd, wd, y=y, ws=ws, accumulate=True)
+        ref = dl.oracle_y(x_h, ids, w, shared=True)
+        torch.cuda.synchronize()
+        assert_close(y.cpu().numpy() - y0.cpu().numpy(), ref, "accumulate " + fn.__name__)
 
 
 @pytest.mark.parametrize("packed", [False, True])
