@@ -214,12 +214,13 @@ struct Args {
     const float* w;      // [n*m]
     float* y;            // [n][d]
     char* h;             // bf16: hi [nslot][d_ff] then lo [nslot][d_ff]; fp32: [nslot][d_ff]
-    float* O;            // [nslot][d]
+    float* O;            // [nslot][ks][d]: per slot and contraction part
     int32_t* sync;       // counters, see layout above
     int32_t* info;       // optional [3]
     int32_t n, m, N, d, d_ff;
     int32_t units, T1, T2;
     int32_t units_r;     // routed units; units units_r .. units-1 are the shared experts
+    int32_t ks;          // down items per (unit, row tile): parts of the d_ff contraction
     int32_t n_shared;
     int32_t nslot;       // rows of h and O: routed slots t*m + j, then shared slots nm + s*n + t
     int32_t accumulate;
@@ -404,8 +405,14 @@ __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e,
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) bx[slot][tt] = bload2<0>(rx, st.vofs(lx[tt], j), so);
         };
+        // the ring's first loads in slot order (a scheduling barrier after each slot):
+        // the loop's waits then count only the other half's loads as outstanding,
+        // instead of waiting for every load whenever the prologue order differs
 #pragma unroll
-        for (int i = 0; i < P; ++i) issue(i, i);
+        for (int i = 0; i < P; ++i) {
+            issue(i, i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         f32x4 accg[RB][NT], accu[RB][NT];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -611,7 +618,8 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
         if (want_status && cur < 0) resolve(0, true, e, g, sh);  // an empty share still reports the status
     } else {
         const int item = (int)blockIdx.x - a.g1;
-        const int u = item / a.T2, t = item - u * a.T2;
+        const int ut = item / a.ks, kp = item - ut * a.ks;  // contraction part kp of (unit, row tile)
+        const int u = ut / a.T2, t = ut - u * a.T2;
         int32_t* hcnt = a.sync + kLine * u;      // this unit's h-ready count
         int32_t* dcnt = hcnt + 1;                // this unit's finished down items
         int32_t* ocnt = a.sync + kLine * (MOE_MAX_SLOTS + t);  // arrivals on this down tile
@@ -626,10 +634,13 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
             const uint32_t hbytes = (uint32_t)nslot * a.d_ff * F::kEsize;
             const auto rh = rsrc(a.h, hbytes);
             const auto rl = rsrc(a.h + (BF16 ? hbytes : 0), hbytes);
-            const auto ro = rsrc(a.O, (uint32_t)nslot * a.d * 4);
+            const auto ro = rsrc(a.O, (uint32_t)nslot * a.ks * a.d * 4);
+            // steps kb .. ke-1 of the d_ff contraction (all of it when ks == 1), split
+            // over the four waves
             const int S = (a.d_ff + F::kStep - 1) / F::kStep;
-            const int s0 = wave * S / kWaves;
-            const Steps<BF16, KF> st{s0, (wave + 1) * S / kWaves - s0, a.d_ff, q};
+            const int kb = kp * S / a.ks, kl = (kp + 1) * S / a.ks - kb;
+            const int s0 = kb + wave * kl / kWaves;
+            const Steps<BF16, KF> st{s0, kb + (wave + 1) * kl / kWaves - s0, a.d_ff, q};
             const PSteps<BF16, KF> pst{s0, st.ns, a.d_ff, a.d, q};  // W_down packed (PK)
             const int ns = st.ns;
             uint32_t lrow[RB2];
@@ -718,7 +729,8 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
                         const int i0 = t * RT2 + rb * kTile + 4 * q;
                         if (col_ok && i0 < a.d)  // d % 8 == 0: rows i0..i0+3 all valid
                             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro,
-                                                                   ((uint32_t)sm.grp[cb + lr] * a.d + i0) * 4, 0, kSc1);
+                                                                   (((uint32_t)sm.grp[cb + lr] * a.ks + kp) * a.d + i0) * 4, 0,
+                                                                   kSc1);
                         stores_complete();
                     }
                     __syncthreads();
@@ -740,7 +752,10 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
                     }
                 };
 #pragma unroll
-                for (int i = 0; i < P; ++i) issue_a(i, i);  // weights first
+                for (int i = 0; i < P; ++i) {  // weights first, in slot order (see gate_up)
+                    issue_a(i, i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 if (base == 0) {
                     if (tid == 0 && !wait_count(hcnt, a.T1) && a.info) a.info[2] = MOE_E_HIP;
                     __syncthreads();  // h loads (sc1) below are issued after the count was seen
@@ -751,7 +766,10 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
                     lh[tt] = st.lane_base(gi < g ? (uint32_t)sm.grp[gi] * a.d_ff * F::kEsize : kOOB);
                 }
 #pragma unroll
-                for (int i = 0; i < P; ++i) issue_b(i, i);
+                for (int i = 0; i < P; ++i) {
+                    issue_b(i, i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 f32x4 acc[RB2][NT];
 #pragma unroll
                 for (int rb = 0; rb < RB2; ++rb)
@@ -792,14 +810,14 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
                     const int i0 = t * RT2 + rb * kTile + 4 * q;
                     if (gi < g && i0 < a.d)  // d % 8 == 0: rows i0..i0+3 all valid
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro,
-                                                               ((uint32_t)sm.grp[gi] * a.d + i0) * 4, 0, kSc1);
+                                                               (((uint32_t)sm.grp[gi] * a.ks + kp) * a.d + i0) * 4, 0, kSc1);
                     stores_complete();
                 }
                 __syncthreads();
             }
             // the unit's last down item resets the unit's counters for the next call
             // (every down item of the unit has seen the full h-ready count by now)
-            if (tid == 0 && atomicAdd(dcnt, 1) == a.T2 - 1) {
+            if (tid == 0 && atomicAdd(dcnt, 1) == a.T2 * a.ks - 1) {
                 __hip_atomic_store(hcnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(dcnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -807,51 +825,54 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
         // arrival on this row tile; the last unit to arrive combines its rows
         if (tid == 0) {
             const int old = atomicAdd(ocnt, 1);  // after the writers' completed stores and the barrier
-            s_last = old == a.units - 1;
+            s_last = old == a.units * a.ks - 1;
             if (s_last) __hip_atomic_store(ocnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // all arrived
         }
         __syncthreads();  // O loads (sc1) below are issued after the last arrival was seen
         if (s_last) {
-            // y_t = sum_j w_tj O_tj + sum_s O_(shared s, t) for 4 rows per thread,
-            // slots in increasing j, then shared experts in increasing s; the O loads
-            // (sc1) of up to kCJ slots are in flight together
+            // y_t = sum_j w_tj sum_p O_(tj, p) + sum_s sum_p O_(shared s, t, p) for 4 rows
+            // per thread: slots in increasing j, then shared experts in increasing s,
+            // each slot's contraction parts p in increasing order (w_tj applied to each
+            // part); the O loads (sc1) of up to kCJ (slot, part) pairs are in flight
+            // together
             constexpr int kCJ = 8;
+            const int ks = a.ks;
             const int i0 = t * RT2;
             const int q4 = min(RT2, a.d - i0) / 4;  // d % 8 == 0
-            const auto rO = rsrc(a.O, (uint32_t)(SH ? a.nslot : nm) * a.d * 4);
+            const auto rO = rsrc(a.O, (uint32_t)(SH ? a.nslot : nm) * ks * a.d * 4);
+            const int nr = a.m * ks;                                  // routed (slot, part) pairs of a token
+            const int npair = nr + (SH ? a.n_shared * ks : 0);        // and the shared experts' pairs
             for (int o = tid; o < a.n * q4; o += kThreads) {
                 const int tok = o / q4, i = i0 + 4 * (o - tok * q4);
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-                for (int j0 = 0; j0 < a.m; j0 += kCJ) {
+                for (int c0 = 0; c0 < npair; c0 += kCJ) {
                     u32x4 ov[kCJ];
                     float wv[kCJ];
                     bool ok[kCJ];
 #pragma unroll
                     for (int jj = 0; jj < kCJ; ++jj) {
-                        const int s = tok * a.m + j0 + jj;
-                        const int id = j0 + jj < a.m ? a.ids[s] : -1;
-                        ok[jj] = id >= 0 && id < a.N;
-                        wv[jj] = ok[jj] ? a.w[s] : 0.f;
-                        ov[jj] = bload_sc1(rO, ok[jj] ? ((uint32_t)s * a.d + i) * 4 : kOOB);
+                        const int c = c0 + jj;
+                        int sl = -1;
+                        float wgt = 1.f;
+                        if (c < nr) {
+                            const int s = tok * a.m + c / ks;
+                            const int id = a.ids[s];
+                            if (id >= 0 && id < a.N) {
+                                sl = s;
+                                wgt = a.w[s];
+                            }
+                        } else if (SH && c < npair) {
+                            sl = nm + ((c - nr) / ks) * a.n + tok;
+                        }
+                        ok[jj] = sl >= 0;
+                        wv[jj] = wgt;
+                        ov[jj] = bload_sc1(rO, ok[jj] ? (((uint32_t)sl * ks + c % ks) * a.d + i) * 4 : kOOB);
                     }
 #pragma unroll
                     for (int jj = 0; jj < kCJ; ++jj)
                         if (ok[jj])
 #pragma unroll
                             for (int r = 0; r < 4; ++r) acc[r] = fmaf(wv[jj], __uint_as_float(ov[jj][r]), acc[r]);
-                }
-                for (int s0 = 0; SH && s0 < a.n_shared; s0 += kCJ) {
-                    u32x4 ov[kCJ];
-#pragma unroll
-                    for (int ss = 0; ss < kCJ; ++ss) {
-                        const int sl = nm + (s0 + ss) * a.n + tok;
-                        ov[ss] = bload_sc1(rO, s0 + ss < a.n_shared ? ((uint32_t)sl * a.d + i) * 4 : kOOB);
-                    }
-#pragma unroll
-                    for (int ss = 0; ss < kCJ; ++ss)
-                        if (s0 + ss < a.n_shared)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) acc[r] += __uint_as_float(ov[ss][r]);
                 }
                 f32x4* yp = reinterpret_cast<f32x4*>(a.y + (size_t)tok * a.d + i);
                 *yp = a.accumulate ? *yp + acc : acc;
@@ -974,6 +995,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+constexpr int kMaxKs = 4;  // contraction parts of a streaming down item
+
 int check_desc(const moe_layer_desc* d, int32_t n) {
     if (!d) return MOE_E_INVAL;
     if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_E_DTYPE;
@@ -990,12 +1013,13 @@ int check_desc(const moe_layer_desc* d, int32_t n) {
     if (d->n_shared < 0 || d->n_shared > MOE_MAX_SHARED) return MOE_E_INVAL;
     if ((int64_t)n * d->m + d->n_shared > MOE_MAX_SLOTS) return MOE_E_INVAL;
     const int64_t nslot = (int64_t)n * d->m + (int64_t)d->n_shared * n;
-    if (nslot * d->d_ff * 4 > (1ll << 31) - 4096 || nslot * d->d_model * 4 > (1ll << 31) - 4096) return MOE_E_INVAL;
+    if (nslot * d->d_ff * 4 > (1ll << 31) - 4096 || nslot * kMaxKs * d->d_model * 4 > (1ll << 31) - 4096)
+        return MOE_E_INVAL;
     return MOE_OK;
 }
 
 struct Plan {
-    int units, units_r, nslot, T1, T2, nt, rb;
+    int units, units_r, nslot, T1, T2, nt, rb, ks;
     int g1, S1;  // gate/up work groups, K steps per gate/up tile
     size_t part_off;
     bool dpf;    // down items in register mode
@@ -1044,6 +1068,12 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     p.lds = p.dpf ? (size_t)p.gl * per_tok : 0;
     const int rb2 = p.dpf ? 1 : p.rb;
     p.T2 = (d->d_model + kTile * rb2 - 1) / (kTile * rb2);
+    // Streaming down items (not register mode) each stream their rows' W_down after
+    // the wait, at what one work group keeps in flight; with fewer than 4 items per
+    // compute unit the d_ff contraction of each (unit, row tile) is cut into ks
+    // parts, one item each, summed in the combine.
+    const int64_t ditems = (int64_t)p.units * p.T2;
+    p.ks = p.dpf ? 1 : (int)std::min<int64_t>(kMaxKs, std::max<int64_t>(1, (4 * kCUs + ditems - 1) / ditems));
     // Gate/up work is cut into kCUs equal shares when there are between half and
     // twice as many tiles as compute units: then no compute unit holds two tiles
     // while another holds one.  With fewer tiles than half the compute units (a
@@ -1061,7 +1091,7 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     p.sync_off = 0;
     p.h_off = (size_t)kSyncWords * 4;
     p.o_off = p.h_off + align_up((size_t)p.nslot * d->d_ff * 4);
-    p.part_off = p.o_off + align_up((size_t)p.nslot * d->d_model * 4);
+    p.part_off = p.o_off + align_up((size_t)p.nslot * p.ks * d->d_model * 4);
     p.total = p.part_off + (split ? align_up((size_t)part_bytes) : 0);
     return p;
 }
@@ -1155,12 +1185,13 @@ int run_expert(const moe_layer_desc* d, const moe_layer_weights* W, const void* 
     args.nslot = p.nslot;
     args.T1 = p.T1;
     args.T2 = p.T2;
+    args.ks = p.ks;
     args.accumulate = (d->flags & MOE_FLAG_ACCUMULATE) ? 1 : 0;
     args.gl = p.gl;
     args.g1 = p.g1;
     args.S1 = p.S1;
     args.part = reinterpret_cast<float*>(wsb + p.part_off);
-    const int grid = p.g1 + p.units * p.T2;
+    const int grid = p.g1 + p.units * p.T2 * p.ks;
     (void)hipGetLastError();
     if (events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(events[0]), st);
     const bool bf = d->dtype == MOE_BF16;

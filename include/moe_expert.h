@@ -118,7 +118,9 @@ int moe_route_group(const int32_t* ids, int32_t n, int32_t m, int32_t N, int32_t
  * invalid arguments.  For a pass of k tokens with S = k*m + n_shared*k slots (the
  * routed slots, then one per token and shared expert) the workspace holds 224 KB
  * of synchronisation counters (one per 128-byte line), the slots' hidden
- * activations and expert outputs (S*(d_ff + d_model)*4 bytes) and, when the
+ * activations (S*d_ff*4 bytes), their expert outputs (S*P*d_model*4 bytes, P = 1..4
+ * parts of the d_ff contraction; P > 1 only for passes with few down-projection
+ * work items and d_ff too long to keep in registers) and, when the
  * pass's gate/up work is fewer than 511 row tiles, the partial sums of tiles that
  * work groups share (3*S*d_ff*8 bytes), each piece aligned to 256 bytes.  The
  * size returned is the largest over k = 1..n, so a workspace sized for n serves

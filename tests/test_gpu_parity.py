@@ -110,12 +110,12 @@ def test_tiny_fp32_many_seeds(packed):
 @pytest.mark.parametrize("N,m,d,d_ff,n", [
     (5, 3, 72, 136, 1), (5, 3, 72, 136, 3), (5, 3, 72, 136, 17), (6, 2, 40, 24, 33),
     (4, 4, 8, 8, 64), (12, 4, 264, 200, 64), (9, 1, 1032, 40, 20),
-    # d_ff too long for the down weights to sit in registers: the streaming down path
-    (7, 2, 136, 1560, 5), (7, 2, 136, 1560, 40),
+    # d_ff too long for the down weights to sit in registers: the streaming down path,
+    # with few down items each (unit, row tile) cut into 4 parts of the d_ff contraction
+    (7, 2, 136, 1560, 5), (7, 2, 136, 1560, 40), (3, 2, 64, 2048, 2), (3, 1, 1024, 1040, 1),
     # 128..1024 gate/up tiles: K ranges shared between work groups (split tiles)
     (40, 4, 72, 1000, 3), (40, 4, 200, 520, 5),
-    # multiples of 32: the fused pass with packed W_down (n <= 8), several shares per unit
-    # and units per share, blocks cut by share boundaries
+    # multiples of 32, fewer tiles than half the compute units (each tile cut in two)
     (6, 3, 96, 160, 1), (6, 3, 96, 160, 8), (33, 8, 256, 64, 7), (4, 4, 64, 96, 8), (12, 6, 512, 352, 5)])
 @pytest.mark.parametrize("packed", [False, True])
 def test_ragged_shapes(dtype, N, m, d, d_ff, n, packed):
