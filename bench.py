@@ -21,6 +21,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -210,6 +211,85 @@ def write_profile_summary(prof_dir, bench_json, config):
     path = os.path.join(ROOT, "profiles", "k_expert_%s_n1-8.md" % config)
     open(path, "w").write("\n".join(lines) + "\n")
     print(path)
+
+
+def chosen_id_section(args, efa, routing, spec, layer, ws, ys, flush, ev, stream, recs, per_kind, x_of):
+    """Passes with chosen ids (U distinct experts among n m slots, from heavy
+    repetition to none, n = 2..9), the fits of Eq. (4) and Eq. (E.1) through the
+    library, the re-read cost c_re/c_u, each fit's median relative error on the
+    timed windows of recorded-style routing (epsilon, the larger of the two) and
+    the Table 2 factors applied to the measured passes."""
+    import torch
+    m, N, b = spec.m, spec.N, spec.expert_bytes
+    e2 = ev.make(2)
+    rows = []
+    for n in range(2, 10):
+        Us = sorted(set(int(round(v)) for v in np.linspace(m, min(n * m, N), 6)))
+        x = x_of(n)
+        y = torch.empty(n, spec.d, dtype=torch.float32, device="cuda")
+        for U in Us:
+            for rep in range(3):
+                tr = routing.chosen_pass(N, m, n, U, routing.rng_for(args.seed, 0, "chosen", 1000 * n + 10 * U + rep))
+                ids = torch.from_numpy(tr.ids).cuda()
+                w = torch.from_numpy(tr.w).cuda()
+                t = {}
+                for kname, fn in (("slot", efa.expert_perslot), ("dedup", efa.expert_dedup)):
+                    tl = []
+                    for _ in range(3):
+                        flush()
+                        fn(layer, x, ids, w, y=y, ws=ws, stream=stream, events=e2)
+                        tl.append(ev.ms(e2[0], e2[1]) * 1e-3)
+                    t[kname] = float(np.median(tl))
+                rows.append((n, U, t["slot"], t["dedup"]))
+    n_c = np.array([r[0] for r in rows]); U_c = np.array([r[1] for r in rows])
+    cs = efa.fit_times(efa.MOE_KIND_SLOT, n_c, U_c, m, np.array([r[2] for r in rows]), b)
+    cd = efa.fit_times(efa.MOE_KIND_DEDUP, n_c, U_c, m, np.array([r[3] for r in rows]), b)
+    # each fit's relative error on the timed windows (n >= 2)
+    win = [r for r in recs if r["n"] >= 2]
+    nw = np.array([r["n"] for r in win], np.float64); Uw = np.array([r["U"] for r in win], np.float64)
+    pred_s = cs[0] + cs[1] * Uw * b + cs[2] * (nw * m - Uw) * b
+    pred_d = cd[0] + cd[1] * Uw * b + cd[2] * nw
+    meas_s = np.array([r["t_slot_ms"] * 1e-3 for r in win]); meas_d = np.array([r["t_dedup_ms"] * 1e-3 for r in win])
+    eps_s = float(np.median(np.abs(pred_s - meas_s) / meas_s))
+    eps_d = float(np.median(np.abs(pred_d - meas_d) / meas_d))
+    eps = max(eps_s, eps_d)
+    out = {"workload": "passes with chosen ids, n = 2..9, U from m to min(n m, N) (6 values), 3 passes each, "
+                       "median of 3 timed runs after the flush",
+           "passes": [dict(n=int(r[0]), U=int(r[1]), t_slot_us=round(r[2] * 1e6, 2), t_dedup_us=round(r[3] * 1e6, 2))
+                      for r in rows],
+           "fit_slot": {"t_op_us": cs[0] * 1e6, "c_u_s_per_GB": cs[1] * 1e9, "c_re_s_per_GB": cs[2] * 1e9,
+                        "reread_cost": cs[2] / cs[1]},
+           "fit_dedup": {"t_op_us": cd[0] * 1e6, "c_g_s_per_GB": cd[1] * 1e9, "c_t_us_per_token": cd[2] * 1e6},
+           "eps_slot": eps_s, "eps_dedup": eps_d, "eps": eps, "windows": len(win)}
+    if eps < 0.5:
+        f = efa.error_bounds(eps)
+        out["bounds"] = f
+        dec = {}
+        for kind, pk in per_kind.items():
+            per_n = pk["per_n"]
+            rows_k = []
+            for row in per_n:
+                if row["n"] < 2:
+                    continue
+                S = row["us_slot"] - row["us_dedup"]
+                rows_k.append(dict(n=row["n"], faster_kernel_decided=bool(abs(math.log(row["r"]) - math.log(row["u"]))
+                                                                         > f["faster_margin"]),
+                                   saving_us=round(S, 2),
+                                   saving_bound_us=round(f["time_factor"] * (row["us_slot"] + row["us_dedup"]), 2)))
+            sm = pk["step_model"]
+            stable = []
+            for key in ("tau_us_slot", "tau_us_dedup"):
+                V = [sm["tau_us_slot"][0]] + sm[key][1:]  # V(0) = the per-slot tau(1), V(k) = tau_p(k+1)
+                cnt = 0
+                for a in A_GRID:
+                    T = [sum(a ** i for i in range(k + 1)) / V[k] for k in range(len(V))]
+                    ks = int(np.argmax(T))
+                    cnt += all(T[i] < f["regret_factor"] * T[ks] for i in range(len(T)) if i != ks)
+                stable.append(cnt)
+            dec[kind] = {"per_n": rows_k, "kstar_certain_slot": stable[0], "kstar_certain_dedup": stable[1],
+                         "a_points": len(A_GRID)}
+        out["decisions"] = dec
+    return out
 
 
 A_GRID = [i / 21.0 for i in range(22)]  # acceptance values of the best-draft-length staircase
@@ -599,6 +679,12 @@ def main():
 
     cpu = cpu_baseline(spec, host_w, host_passes, args.cpu_budget)
     extras = {}
+    if not args.no_extras and args.config == "dsv2lite":
+        ws9 = layer.workspace(9)
+        extras["chosen_ids"] = chosen_id_section(
+            args, efa, routing, spec, layer, ws9, ys, flush, ev, stream, recs, per_kind,
+            lambda n: to_torch(synth.pass_x(spec, args.seed, 0, 77000 + n, n)))
+        del ws9
     if spec.n_shared:
         extras["shared_experts"] = {"workload": "%d always-on shared experts, weight 1, every token: one "
                                                 "deduplicating call per pass (the D(n) bytes of the step model)"

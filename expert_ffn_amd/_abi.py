@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_E_INVAL", -2: "MOE_E_DTYPE", -3: "MOE_E_WO
 # every symbol the header declares
 EXPORTS = ("moe_route_group", "moe_workspace_bytes", "moe_expert_perslot", "moe_expert_dedup",
            "moe_kernels_per_call", "moe_expert_perslot_ev", "moe_expert_dedup_ev", "bytes_requested",
-           "step_time_model", "moe_pack_w_down")
+           "step_time_model", "moe_pack_w_down", "moe_fit_times", "moe_error_bounds")
 
 
 class MoeError(RuntimeError):
@@ -99,6 +99,12 @@ def lib():
             L.step_time_model.restype = ctypes.c_int
             L.moe_pack_w_down.argtypes = [pdesc, vp, vp, vp]
             L.moe_pack_w_down.restype = ctypes.c_int
+            pi32, pd = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)
+            L.moe_fit_times.argtypes = [ctypes.c_int32, ctypes.c_int32, pi32, pi32, ctypes.c_int32, pd,
+                                        ctypes.c_double, pd]
+            L.moe_fit_times.restype = ctypes.c_int
+            L.moe_error_bounds.argtypes = [ctypes.c_double, pd]
+            L.moe_error_bounds.restype = ctypes.c_int
             _LIB = L
     return _LIB
 

@@ -1,10 +1,13 @@
-// Host-side byte accounting and step-time model (double precision).
+// Host-side byte accounting, step-time model, fits and error bounds (double precision).
 //
 // Lan, arXiv:2610.34440:
 //   Section 1 "Bytes":  per-slot requests n m w, deduplicating requests X(n) w.
 //   Section 1 "Speculative decoding", Section 3.1 Eq. (5)-(6), Section 3.2
 //   Eqs. (8)-(9), Section 3.3 and Appendix B.3 (staircase, step points (B.31),
 //   convex case (B.36)), Section 3.4 Eqs. (14) and (16).
+//   Section 2 Eq. (4) and Appendix E Eq. (E.1): least-squares fits of the kernels'
+//   times over passes with chosen ids.  Section 3.5, Table 2 and Appendix C: the
+//   error bounds for a relative bandwidth error eps.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -154,6 +157,82 @@ int step_time_model(const moe_step_in* in, moe_step_out* out) {
             out->rho_star_bytes[ia][k] = 1.0 - (Gm1 * V0b - dD) / (mW * k);
         }
     }
+    return MOE_OK;
+}
+
+// Least squares min |A c - t| for A with three columns (count rows, row-major),
+// by Householder reflections on the column-scaled matrix.  Returns false when a
+// column is (numerically) dependent on the others.
+static bool lsq3(std::vector<double>& A, std::vector<double>& t, int count, double* c) {
+    double scale[3];
+    for (int j = 0; j < 3; ++j) {
+        double mx = 0.0;
+        for (int r = 0; r < count; ++r) mx = fmax(mx, fabs(A[r * 3 + j]));
+        if (!(mx > 0.0)) return false;
+        scale[j] = mx;
+        for (int r = 0; r < count; ++r) A[r * 3 + j] /= mx;
+    }
+    double R[3][3] = {};
+    for (int j = 0; j < 3; ++j) {
+        double nrm = 0.0;
+        for (int r = j; r < count; ++r) nrm += A[r * 3 + j] * A[r * 3 + j];
+        nrm = sqrt(nrm);
+        if (!(nrm > 1e-12)) return false;
+        const double alpha = A[j * 3 + j] > 0.0 ? -nrm : nrm;
+        // v = x - alpha e_1, stored in place; H = I - 2 v v^T / (v^T v)
+        A[j * 3 + j] -= alpha;
+        double vv = 0.0;
+        for (int r = j; r < count; ++r) vv += A[r * 3 + j] * A[r * 3 + j];
+        for (int jj = j + 1; jj < 3; ++jj) {
+            double dot = 0.0;
+            for (int r = j; r < count; ++r) dot += A[r * 3 + j] * A[r * 3 + jj];
+            const double f = 2.0 * dot / vv;
+            for (int r = j; r < count; ++r) A[r * 3 + jj] -= f * A[r * 3 + j];
+        }
+        double dot = 0.0;
+        for (int r = j; r < count; ++r) dot += A[r * 3 + j] * t[r];
+        const double f = 2.0 * dot / vv;
+        for (int r = j; r < count; ++r) t[r] -= f * A[r * 3 + j];
+        R[j][j] = alpha;
+        for (int jj = j + 1; jj < 3; ++jj) R[j][jj] = A[j * 3 + jj];
+    }
+    for (int j = 2; j >= 0; --j) {
+        double v = t[j];
+        for (int jj = j + 1; jj < 3; ++jj) v -= R[j][jj] * c[jj];
+        c[j] = v / R[j][j];
+    }
+    for (int j = 0; j < 3; ++j) c[j] /= scale[j];
+    return true;
+}
+
+int moe_fit_times(int32_t kind, int32_t count, const int32_t* n, const int32_t* U, int32_t m, const double* t,
+                  double b, double* coef) {
+    if (kind != MOE_KIND_SLOT && kind != MOE_KIND_DEDUP) return MOE_E_INVAL;
+    if (!n || !U || !t || !coef || count < 3 || count > (1 << 24) || m < 1 || !(b > 0.0) || !isfinite(b))
+        return MOE_E_INVAL;
+    std::vector<double> A((size_t)count * 3), y((size_t)count);
+    for (int r = 0; r < count; ++r) {
+        if (n[r] < 1 || U[r] < 1 || (int64_t)U[r] > (int64_t)n[r] * m || !isfinite(t[r])) return MOE_E_INVAL;
+        A[r * 3 + 0] = 1.0;
+        A[r * 3 + 1] = (double)U[r] * b;
+        A[r * 3 + 2] = kind == MOE_KIND_SLOT ? ((double)n[r] * m - U[r]) * b : (double)n[r];
+        y[r] = t[r];
+    }
+    double c[3];
+    if (!lsq3(A, y, count, c)) return MOE_E_INVAL;
+    for (int j = 0; j < 3; ++j) coef[j] = c[j];
+    return MOE_OK;
+}
+
+int moe_error_bounds(double eps, double* out) {
+    if (!out || !(eps >= 0.0) || !(eps < 0.5)) return MOE_E_INVAL;
+    const double f = eps / (1.0 - eps);
+    const double delta = f;
+    out[0] = f;                                    // (17), (18)
+    out[1] = log((1.0 + eps) / (1.0 - eps));       // (19)
+    out[2] = delta;                                // from eps to delta
+    out[3] = (1.0 - delta) / (1.0 + delta);        // (20)
+    out[4] = (1.0 + delta) / (1.0 - delta);        // (21)
     return MOE_OK;
 }
 

@@ -239,3 +239,27 @@ def step_time_model(n_max, a, m_W, E, beta, t0=0.0, D=0.0, kv=None, beta_D=1.0, 
         "rho_star": np.array(so.rho_star)[:na, :n_max].copy(),
         "rho_star_bytes": np.array(so.rho_star_bytes)[:na, :n_max].copy(),
     }
+
+
+def fit_times(kind, n, U, m, t, b):
+    """Least-squares fit of a kernel's times over passes with chosen ids
+    (``moe_fit_times``): per-slot (t_op, c_u, c_re), deduplicating (t_op, c_g, c_t)."""
+    n = np.ascontiguousarray(n, dtype=np.int32)
+    U = np.ascontiguousarray(U, dtype=np.int32)
+    t = np.ascontiguousarray(t, dtype=np.float64)
+    if not (n.shape == U.shape == t.shape and n.ndim == 1):
+        raise ValueError("n, U and t must be 1-d arrays of one length")
+    coef = np.zeros(3, np.float64)
+    pi32, pd = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)
+    st = lib().moe_fit_times(int(kind), int(n.size), n.ctypes.data_as(pi32), U.ctypes.data_as(pi32), int(m),
+                             t.ctypes.data_as(pd), float(b), coef.ctypes.data_as(pd))
+    check("moe_fit_times", st)
+    return tuple(float(c) for c in coef)
+
+
+def error_bounds(eps):
+    """Factors of the Table 2 bounds for a relative bandwidth error eps (``moe_error_bounds``)."""
+    out = np.zeros(5, np.float64)
+    check("moe_error_bounds", lib().moe_error_bounds(float(eps), out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
+    return {"time_factor": float(out[0]), "faster_margin": float(out[1]), "delta": float(out[2]),
+            "regret_factor": float(out[3]), "speedup_factor": float(out[4])}

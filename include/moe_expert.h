@@ -273,6 +273,38 @@ typedef struct {
 
 int step_time_model(const moe_step_in* in, moe_step_out* out);
 
+/*
+ * moe_fit_times -- least-squares fit of one kernel's measured times over passes
+ * with chosen ids (paper Section 2; a pass of n tokens whose n*m slots name U
+ * distinct experts), host only, double:
+ *   MOE_KIND_SLOT  (Eq. 4):   t = t_op + c_u U b + c_re (n m - U) b   coef = (t_op, c_u, c_re)
+ *   MOE_KIND_DEDUP (Eq. E.1): t = t_op + c_g U b + c_t n             coef = (t_op, c_g, c_t)
+ * b = bytes of one expert of the timed layer.  c_re / c_u is the re-read cost: 1
+ * when a repeated slot is read again from memory, near 0 when a cache serves it.
+ *   n, U, t  host [count]; 1 <= U[i] <= n[i] m; t in any fixed time unit
+ *   coef     host [3], written on success
+ * Householder QR on the column-scaled system.  Returns MOE_OK, or MOE_E_INVAL for
+ * bad arguments, count < 3, or passes that do not determine all three constants.
+ */
+int moe_fit_times(int32_t kind, int32_t count, const int32_t* n, const int32_t* U, int32_t m,
+                  const double* t, double b, double* coef);
+
+/*
+ * moe_error_bounds -- the factors of the bounds of paper Table 2 (Section 3.5,
+ * Appendix C) for a relative bandwidth error |e| <= eps, 0 <= eps < 1/2, host only:
+ *   out[0] = eps/(1-eps): (17) |tau^_p(n) - tau_p(n)| <= out[0] M_p(n) <= out[0] tau_p(n);
+ *            (18) |S^(n) - S(n)| <= out[0] (M^e_slot(n) + M^e_dedup(n))
+ *   out[1] = ln((1+eps)/(1-eps)): (19) the predicted faster kernel is the true one
+ *            when |ln r(n) - ln u(n)| > out[1]
+ *   out[2] = delta = eps/(1-eps), the relative step-time error from bandwidth errors
+ *   out[3] = (1-delta)/(1+delta): (20) T_a(k^*) >= out[3] T_a(k*), and k^* = k* when
+ *            T_a(i) < out[3] T_a(k*) for every i != k*
+ *   out[4] = (1+delta)/(1-delta) = 1/(1-2 eps): (21) the predicted best speedup is
+ *            within [1/out[4], out[4]] times the true one
+ * Returns MOE_OK or MOE_E_INVAL.
+ */
+int moe_error_bounds(double eps, double* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,12 @@ Readings used where the workload descriptions leave a step open:
 * ``tree``: 32 verified nodes, node 0 the current token, node 1 its single
   child, every node at depths 1..4 with two children; node ids breadth first
   (parents before children); node 0 uniform, every other node drawn from its
-  parent by the ``correlated`` rule.
+  parent by the ``correlated`` rule;
+* ``chosen`` (passes with chosen ids): the n m slots of a pass name exactly U
+  distinct experts, m <= U <= min(n m, N), a seeded U-subset of the N; token 0
+  takes m of them, the other U - m are spread as evenly as possible over tokens
+  1..n-1 in order, and each token fills its other slots with distinct experts
+  that earlier tokens named; weights from fresh N(0,1) logits.
 """
 from collections import namedtuple
 
@@ -107,6 +112,24 @@ def tree_routing(N, m, p, rng):
     logits = rng.standard_normal((parents.size, m))
     tr = _finish(rows, logits)
     return parents, tr
+
+
+def chosen_pass(N, m, n, U, rng):
+    """One pass of n tokens whose slots name exactly U distinct experts."""
+    if not (1 <= m <= N and n >= 1 and m <= U <= min(n * m, N)):
+        raise ValueError("need m <= U <= min(n m, N)")
+    experts = [int(e) for e in rng.choice(N, size=U, replace=False)]
+    fresh = experts[m:]
+    rows = [experts[:m]]
+    named = list(experts[:m])
+    for t in range(1, n):
+        k = -(-len(fresh) // (n - t))  # new experts this token: ceil(remaining / tokens left)
+        new, fresh = fresh[:k], fresh[k:]
+        old = [int(e) for e in rng.choice(named, size=m - k, replace=False)] if m > k else []
+        rows.append(new + old)
+        named += new
+    logits = rng.standard_normal((n, m))
+    return _finish(rows, logits)
 
 
 def make_trace(spec, kind, T, seed, layer=0, p=None, s=None):

@@ -3,6 +3,7 @@ import math
 from math import comb
 
 import numpy as np
+import pytest
 import torch
 
 import synth
@@ -88,3 +89,20 @@ def test_tree_shape():
     assert [depth.count(k) for k in range(6)] == [1, 1, 2, 4, 8, 16]
     _, tr = routing.tree_routing(128, 8, 0.5, routing.rng_for(4, 0, "tree"))
     assert tr.ids.shape == (32, 8)
+
+
+def test_chosen_passes_name_exactly_U_experts():
+    from synth import routing
+    rng = routing.rng_for(3, 0, "chosen")
+    for N, m, n in ((64, 6, 1), (64, 6, 2), (64, 6, 9), (8, 2, 4), (128, 8, 8), (10, 3, 5)):
+        for U in range(m, min(n * m, N) + 1):
+            tr = routing.chosen_pass(N, m, n, U, rng)
+            assert tr.ids.shape == (n, m) and tr.w.shape == (n, m)
+            assert len(set(tr.ids.reshape(-1).tolist())) == U
+            assert all(len(set(r)) == m for r in tr.ids.tolist())
+            assert tr.ids.min() >= 0 and tr.ids.max() < N
+            assert np.allclose(tr.w.sum(axis=1), 1.0, atol=1e-6)
+    with pytest.raises(ValueError):
+        routing.chosen_pass(64, 6, 2, 5, rng)
+    with pytest.raises(ValueError):
+        routing.chosen_pass(8, 2, 8, 9, rng)
