@@ -213,6 +213,32 @@ def write_profile_summary(prof_dir, bench_json, config):
     print(path)
 
 
+def router_section(args, efa, synth, spec, passes, kinds, nvals, flush, ev, stream):
+    """The router ahead of the expert operation (two launches: logits, then top-m and
+    softmax) on the layer's own activations, after the flush, events around both."""
+    import torch
+    from synth.device import to_torch
+    wr = to_torch(synth.router_weights(spec, args.seed))
+    e2 = ev.make(2)
+    us = []
+    for n in nvals:
+        x = passes[(kinds[0][0], n, 0)]["x"]
+        out = efa.router_topk(wr, x, spec.m, stream=stream)
+        tl = []
+        for _ in range(5):
+            flush()
+            ev.record(e2[0], stream.cuda_stream)
+            efa.router_topk(wr, x, spec.m, out=out, stream=stream)
+            ev.record(e2[1], stream.cuda_stream)
+            tl.append(ev.ms(e2[0], e2[1]) * 1e3)
+        us.append(round(float(np.median(tl)), 2))
+    nb = spec.N * spec.d * 2
+    return {"workload": "router of the layer: logits of N=%d experts over d=%d (bf16), top-%d and softmax, n = 1..%d"
+                        % (spec.N, spec.d, spec.m, nvals[-1]),
+            "launches": 2, "us_per_n": us, "router_bytes": nb,
+            "GBps_per_n": [round((nb + n * spec.d * 2) / (t * 1e-6) / 1e9, 1) for n, t in zip(nvals, us)]}
+
+
 def chosen_id_section(args, efa, routing, spec, layer, ws, ys, flush, ev, stream, recs, per_kind, x_of):
     """Passes with chosen ids (U distinct experts among n m slots, from heavy
     repetition to none, n = 2..9), the fits of Eq. (4) and Eq. (E.1) through the
@@ -681,6 +707,7 @@ def main():
     extras = {}
     if not args.no_extras and args.config == "dsv2lite":
         ws9 = layer.workspace(9)
+        extras["router"] = router_section(args, efa, synth, spec, passes, kinds, nvals, flush, ev, stream)
         extras["chosen_ids"] = chosen_id_section(
             args, efa, routing, spec, layer, ws9, ys, flush, ev, stream, recs, per_kind,
             lambda n: to_torch(synth.pass_x(spec, args.seed, 0, 77000 + n, n)))

@@ -10,5 +10,5 @@ from ._abi import (  # noqa: F401
 )
 from .ops import (  # noqa: F401
     Grouping, Layer, bytes_requested, error_bounds, expert_dedup, expert_perslot, fit_times, kernels_per_call,
-    pack_w_down, route_group, step_time_model,
+    pack_w_down, route_group, router_topk, step_time_model,
 )

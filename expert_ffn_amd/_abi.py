@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_E_INVAL", -2: "MOE_E_DTYPE", -3: "MOE_E_WO
 # every symbol the header declares
 EXPORTS = ("moe_route_group", "moe_workspace_bytes", "moe_expert_perslot", "moe_expert_dedup",
            "moe_kernels_per_call", "moe_expert_perslot_ev", "moe_expert_dedup_ev", "bytes_requested",
-           "step_time_model", "moe_pack_w_down", "moe_fit_times", "moe_error_bounds")
+           "step_time_model", "moe_pack_w_down", "moe_fit_times", "moe_error_bounds",
+           "moe_router_topk", "moe_router_workspace_bytes")
 
 
 class MoeError(RuntimeError):
@@ -105,6 +106,10 @@ def lib():
             L.moe_fit_times.restype = ctypes.c_int
             L.moe_error_bounds.argtypes = [ctypes.c_double, pd]
             L.moe_error_bounds.restype = ctypes.c_int
+            L.moe_router_topk.argtypes = [pdesc, vp, vp, ctypes.c_int32, vp, vp, vp, vp, sz, vp]
+            L.moe_router_topk.restype = ctypes.c_int
+            L.moe_router_workspace_bytes.argtypes = [pdesc, ctypes.c_int32]
+            L.moe_router_workspace_bytes.restype = sz
             _LIB = L
     return _LIB
 

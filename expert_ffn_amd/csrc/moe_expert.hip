@@ -881,6 +881,208 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
     }
 }
 
+// ---------------------------------------------------------------------------
+// Router: a router sends each token to m of the N experts (paper Section 1).
+// Logits l_te = W_r[e] . x_t (fp32 accumulation), then per token the m largest
+// logits in descending order (equal logits: lower id first) and their softmax.
+// ---------------------------------------------------------------------------
+constexpr int kRP = 4;      // router: loads of a wave in flight, in steps
+constexpr int kRKS = 4;     // router: most parts of the d contraction
+
+// One workgroup per 16 experts x 16 tokens x one of KS parts of the d
+// contraction; the four waves split the part.  Partial logits go to
+// part[ks][t][e]; the selection kernel adds the parts in order.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_router_logits(const char* __restrict__ wr, const char* __restrict__ x,
+                                                            int N, int n, int d, float* __restrict__ part) {
+    using F = Fmt<BF16>;
+    __shared__ f32x4 red[kWaves][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = uni(tid >> 6);
+    const int lr = lane & 15, q = lane >> 4;
+    const int e0 = blockIdx.x * kTile, t0 = blockIdx.y * kTile;
+    const auto rw = rsrc(wr, (uint32_t)N * d * F::kEsize);
+    const auto rx = rsrc(x, (uint32_t)n * d * F::kEsize);
+    const int S = (d + F::kStep - 1) / F::kStep;
+    const int KS = gridDim.z, ks = blockIdx.z;
+    const int kb = ks * S / KS, kl = (ks + 1) * S / KS - kb;  // this part's steps
+    const int s0 = kb + wave * kl / kWaves, ns = kb + (wave + 1) * kl / kWaves - s0;
+    // this lane's expert row (A operand) and token column (B operand)
+    const uint32_t la = e0 + lr < N ? ((uint32_t)(e0 + lr) * d + q * F::kPer) * F::kEsize : kOOB;
+    const uint32_t lb = t0 + lr < n ? ((uint32_t)(t0 + lr) * d + q * F::kPer) * F::kEsize : kOOB;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i0 = 0; i0 < ns; i0 += kRP) {
+        u32x4 a[kRP], b[kRP];
+#pragma unroll
+        for (int j = 0; j < kRP; ++j) {
+            const int s = s0 + i0 + j;
+            const bool ok = i0 + j < ns && s * F::kStep + q * F::kPer < d;  // d % 8 == 0: whole chunks
+            const uint32_t so = ok ? (uint32_t)s * F::kStep * F::kEsize : 0u;
+            a[j] = bload2<0>(rw, ok ? la : kOOB, so);
+            b[j] = bload2<0>(rx, ok ? lb : kOOB, so);
+        }
+#pragma unroll
+        for (int j = 0; j < kRP; ++j) acc = F::mma(a[j], b[j], acc);
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        const f32x4 v = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+        // lane l holds experts e0 + 4*(l/16) + i for token t0 + l%16
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = e0 + 4 * q + i, t = t0 + lr;
+            if (e < N && t < n) part[((size_t)ks * n + t) * N + e] = v[i];
+        }
+    }
+}
+
+// (v, id) beats (w, jd): larger logit, or equal logits and lower id
+__device__ __forceinline__ bool rk_before(float v, int id, float w, int jd) { return v > w || (v == w && id < jd); }
+
+// One wave per token (four per workgroup, no barriers): the logits (the KS parts
+// added in order, written out), each lane holding experts lane + 64 j; m rounds of
+// a wave-wide selection of the best remaining (logit, id); the softmax of the m
+// selected logits.
+constexpr int kRPerLane = MOE_MAX_EXPERTS / 64;
+
+__global__ __launch_bounds__(kThreads) void k_router_topm(const float* __restrict__ part, int KS, int n, int N, int m,
+                                                          float* __restrict__ logits, int32_t* __restrict__ ids,
+                                                          float* __restrict__ w) {
+    __shared__ float selv[kWaves][MOE_MAX_SLOTS];
+    __shared__ int seli[kWaves][MOE_MAX_SLOTS];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * kWaves + wave;
+    if (t >= n) return;  // whole waves; the kernel has no barrier
+    // every (expert, part) load of the lane in flight at once (out-of-range ones
+    // read zero through the descriptor, no branches), then the sums in part order
+    const auto rp = rsrc(part, (uint32_t)KS * n * N * 4);
+    float pv[kRPerLane][kRKS];
+#pragma unroll
+    for (int j = 0; j < kRPerLane; ++j)
+#pragma unroll
+        for (int ks = 0; ks < kRKS; ++ks) {
+            const int e = lane + 64 * j;
+            const bool ok = e < N && ks < KS;
+            pv[j][ks] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rp, ok ? (((uint32_t)ks * n + t) * N + e) * 4u : kOOB, 0, 0));
+        }
+    float v[kRPerLane];
+#pragma unroll
+    for (int j = 0; j < kRPerLane; ++j) {
+        float s = pv[j][0];
+#pragma unroll
+        for (int ks = 1; ks < kRKS; ++ks)
+            if (ks < KS) s += pv[j][ks];
+        v[j] = s;
+        const int e = lane + 64 * j;
+        if (e < N) logits[(size_t)t * N + e] = s;
+    }
+    uint32_t taken = 0u;  // bit j: expert lane + 64 j already selected
+    for (int r = 0; r < m; ++r) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < kRPerLane; ++j) {
+            const int e = lane + 64 * j;
+            if (e < N && !((taken >> j) & 1u) && rk_before(v[j], e, bv, bi)) {
+                bv = v[j];
+                bi = e;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (rk_before(ov, oi, bv, bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        // every lane now holds the winner; no candidate (only non-finite logits
+        // left) gives id -1, which the expert calls skip
+        if ((unsigned)bi >= (unsigned)N) bi = -1;
+        else if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        if (lane == 0) {
+            selv[wave][r] = bv;
+            seli[wave][r] = bi;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // softmax over the selected logits, the largest first; the wave's sum by a fixed
+    // tree, lane 0's result for all
+    const float top = selv[wave][0];
+    float part_sum = 0.f;
+    for (int j = lane; j < m; j += 64) part_sum += expf(selv[wave][j] - top);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) part_sum += __shfl_xor(part_sum, o, 64);
+    part_sum = __shfl(part_sum, 0, 64);  // one denominator for every lane
+    for (int j = lane; j < m; j += 64) {
+        ids[(size_t)t * m + j] = seli[wave][j];
+        w[(size_t)t * m + j] = expf(selv[wave][j] - top) / part_sum;
+    }
+}
+
+// Selection by rank for up to kRRMaxN experts: one workgroup of 16 waves per 16
+// tokens loads their logits (the KS parts added in order, written out) into LDS and
+// ranks every (token, expert) by the number of experts that come before it (larger
+// logit, or equal logit and lower id): the rank is the expert's position, so the
+// ranks below m are the selection, in order.  One wave per token then takes the
+// softmax of the selected logits.  No rounds: the cost does not grow with m.
+constexpr int kRRW = 16;                 // waves of the ranking workgroup
+constexpr int kRRMaxN = 256, kRRMaxM = 64;
+
+__global__ __launch_bounds__(64 * kRRW) void k_router_rank(const float* __restrict__ part, int KS, int n, int N, int m,
+                                                           float* __restrict__ logits, int32_t* __restrict__ ids,
+                                                           float* __restrict__ w) {
+    __shared__ float lgt[kTile][kRRMaxN];
+    __shared__ float selv[kTile][kRRMaxM];
+    __shared__ int seli[kTile][kRRMaxM];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = blockIdx.x * kTile;
+    const int nt = min(kTile, n - t0);
+    const auto rp = rsrc(part, (uint32_t)KS * n * N * 4);
+    for (int it = tid; it < nt * N; it += 64 * kRRW) {
+        const int t = it / N, e = it - t * N;
+        float pv[kRKS];  // every part's load in flight, then the sum in part order
+#pragma unroll
+        for (int ks = 0; ks < kRKS; ++ks)
+            pv[ks] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rp, ks < KS ? (((uint32_t)ks * n + t0 + t) * N + e) * 4u : kOOB, 0, 0));
+        float v = pv[0];
+#pragma unroll
+        for (int ks = 1; ks < kRKS; ++ks)
+            if (ks < KS) v += pv[ks];
+        lgt[t][e] = v;
+        logits[(size_t)(t0 + t) * N + e] = v;
+    }
+    __syncthreads();
+    for (int it = tid; it < nt * N; it += 64 * kRRW) {
+        const int t = it / N, e = it - t * N;
+        const float v = lgt[t][e];
+        int rank = 0;
+        for (int k = 0; k < N; ++k) rank += rk_before(lgt[t][k], k, v, e) ? 1 : 0;
+        if (rank < m) {
+            selv[t][rank] = v;
+            seli[t][rank] = e;
+        }
+    }
+    __syncthreads();
+    if (wave < nt) {  // softmax of the selected logits, the largest first; lane 0's sum for all
+        const int t = wave;
+        const float top = selv[t][0];
+        float sum = lane < m ? expf(selv[t][lane] - top) : 0.f;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+        sum = __shfl(sum, 0, 64);
+        if (lane < m) {
+            ids[(size_t)(t0 + t) * m + lane] = seli[t][lane];
+            w[(size_t)(t0 + t) * m + lane] = expf(selv[t][lane] - top) / sum;
+        }
+    }
+}
+
 // Packing of W_down into blocks of 8 columns: dst[e][c][i][k] = src[e][i][8c + k].
 // One thread per 16-byte piece of a source row (8 bf16 or 4 fp32 elements).
 __global__ __launch_bounds__(256) void k_pack_wdown(const char* __restrict__ src, char* __restrict__ dst, int64_t N,
@@ -1208,6 +1410,25 @@ int run_expert(const moe_layer_desc* d, const moe_layer_weights* W, const void* 
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 
+// parts of the router's d contraction: about kCUs workgroups, at least one step per wave
+int router_ks(const moe_layer_desc* d, int32_t n) {
+    const int wg = ((d->N + kTile - 1) / kTile) * ((n + kTile - 1) / kTile);
+    const int steps = (d->d_model + (d->dtype == MOE_BF16 ? 32 : 16) - 1) / (d->dtype == MOE_BF16 ? 32 : 16);
+    return std::max(1, std::min(std::min(kRKS, kCUs / wg), steps / kWaves));
+}
+
+int router_check(const moe_layer_desc* desc, int32_t n) {
+    if (!desc) return MOE_E_INVAL;
+    if (desc->dtype != MOE_F32 && desc->dtype != MOE_BF16) return MOE_E_DTYPE;
+    if (desc->d_model < 8 || desc->d_model % 8) return MOE_E_DTYPE;
+    if (desc->N < 1 || desc->N > MOE_MAX_EXPERTS || desc->m < 1 || desc->m > desc->N || desc->m > MOE_MAX_SLOTS)
+        return MOE_E_INVAL;
+    if (n < 1 || n > MOE_MAX_TOKENS) return MOE_E_INVAL;
+    const int64_t es = desc->dtype == MOE_BF16 ? 2 : 4;
+    if ((int64_t)desc->N * desc->d_model * es > (1ll << 31) - 4096) return MOE_E_INVAL;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1253,6 +1474,43 @@ int moe_pack_w_down(const moe_layer_desc* desc, const void* w_down, void* w_down
     hipLaunchKernelGGL(k_pack_wdown, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(hip_stream),
                        reinterpret_cast<const char*>(w_down), reinterpret_cast<char*>(w_down_packed),
                        (int64_t)desc->N, desc->d_model, desc->d_ff, (int)es);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+size_t moe_router_workspace_bytes(const moe_layer_desc* desc, int32_t n) {
+    if (router_check(desc, n) != MOE_OK) return 0;
+    size_t total = 0;  // largest over 1..n tokens
+    for (int32_t k = 1; k <= n; ++k)
+        total = std::max(total, (size_t)router_ks(desc, k) * k * desc->N * 4);
+    return total;
+}
+
+int moe_router_topk(const moe_layer_desc* desc, const void* w_router, const void* x, int32_t n,
+                               float* logits, int32_t* ids, float* w, void* ws, size_t ws_bytes, void* hip_stream) {
+    const int rc = router_check(desc, n);
+    if (rc != MOE_OK) return rc;
+    if (!w_router || !x || !logits || !ids || !w || !ws) return MOE_E_INVAL;
+    if (!aligned16(w_router) || !aligned16(x) || (reinterpret_cast<uintptr_t>(logits) & 3u) ||
+        (reinterpret_cast<uintptr_t>(ws) & 3u))
+        return MOE_E_INVAL;
+    const int KS = router_ks(desc, n);
+    if (ws_bytes < (size_t)KS * n * desc->N * 4) return MOE_E_WORKSPACE;
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    float* part = reinterpret_cast<float*>(ws);
+    const dim3 g1((desc->N + kTile - 1) / kTile, (n + kTile - 1) / kTile, KS);
+    (void)hipGetLastError();
+    if (desc->dtype == MOE_BF16)
+        hipLaunchKernelGGL(k_router_logits<true>, g1, dim3(kThreads), 0, st, reinterpret_cast<const char*>(w_router),
+                           reinterpret_cast<const char*>(x), desc->N, n, desc->d_model, part);
+    else
+        hipLaunchKernelGGL(k_router_logits<false>, g1, dim3(kThreads), 0, st, reinterpret_cast<const char*>(w_router),
+                           reinterpret_cast<const char*>(x), desc->N, n, desc->d_model, part);
+    if (desc->N <= kRRMaxN && desc->m <= kRRMaxM)
+        hipLaunchKernelGGL(k_router_rank, dim3((n + kTile - 1) / kTile), dim3(64 * kRRW), 0, st, part, KS, n, desc->N,
+                           desc->m, logits, ids, w);
+    else
+        hipLaunchKernelGGL(k_router_topm, dim3((n + kWaves - 1) / kWaves), dim3(kThreads), 0, st, part, KS, n,
+                           desc->N, desc->m, logits, ids, w);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 

@@ -122,6 +122,31 @@ def pack_w_down(layer, w_down, out, stream=None):
     return out
 
 
+Routed = namedtuple("Routed", ["ids", "w", "logits", "ws"])
+
+
+def router_topk(w_router, x, m, out=None, stream=None):
+    """The router (``moe_router_topk``): logits [n][N] fp32, the m largest per token
+    (descending, ties to the lower id) and their softmax.  Returns Routed(ids, w,
+    logits, ws); pass it back as ``out`` to reuse its buffers."""
+    N, d = w_router.shape
+    _check_dev("w_router", w_router)
+    _check_dev("x", x, w_router.dtype, (x.shape[0], d))
+    n = x.shape[0]
+    dev = x.device
+    desc = _abi.LayerDesc(N, int(m), d, 8, _dtype_code(w_router), 0, 0)
+    if out is None:
+        nb = lib().moe_router_workspace_bytes(ctypes.byref(desc), n)
+        if nb == 0:
+            raise _abi.MoeError("moe_router_workspace_bytes", _abi.MOE_E_INVAL)
+        out = Routed(torch.empty(n, m, dtype=torch.int32, device=dev), torch.empty(n, m, dtype=torch.float32, device=dev),
+                     torch.empty(n, N, dtype=torch.float32, device=dev), torch.empty(nb, dtype=torch.uint8, device=dev))
+    st = lib().moe_router_topk(ctypes.byref(desc), _vp(w_router), _vp(x), n, _vp(out.logits), _vp(out.ids),
+                               _vp(out.w), _vp(out.ws), out.ws.numel(), _stream(stream))
+    check("moe_router_topk", st)
+    return out
+
+
 def route_group(ids, N, out=None, stream=None):
     """Group the pass's slots by expert (one kernel launch)."""
     _check_dev("ids", ids, torch.int32)

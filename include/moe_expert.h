@@ -184,6 +184,37 @@ int moe_expert_dedup(const moe_layer_desc* desc, const moe_layer_weights* weight
 int moe_pack_w_down(const moe_layer_desc* desc, const void* w_down, void* w_down_packed,
                     void* hip_stream);
 
+/*
+ * moe_router_topk -- the router ahead of the expert operation: it sends each token
+ * to m of the N experts (paper Section 1).  For every token t of the pass:
+ *   logits[t][e] = W_r[e] . x_t                  (fp32 accumulation, e < N)
+ *   ids[t][0..m)  the m largest logits, in descending order; equal logits: lower id first
+ *   w[t][j]       = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the m selected logits
+ *                 (the same weights as a softmax over all N renormalised to the m)
+ * The ids and weights are in the layout the expert calls take.
+ *   desc      N, m, d_model, dtype (d_ff, flags and n_shared are not used);
+ *             m <= MOE_MAX_SLOTS
+ *   w_router  device [N][d_model], dtype of desc, 16-byte aligned
+ *   x         device [n][d_model], 16-byte aligned; 1 <= n <= MOE_MAX_TOKENS
+ *   logits    device [n][N] fp32 (written)
+ *   ids, w    device [n][m] int32 / fp32 (written)
+ *   ws        device workspace of ws_bytes >= moe_router_workspace_bytes(desc, n),
+ *             4-byte aligned: partial logits of up to 16 parts of the d contraction,
+ *             added in a fixed order (no zero-fill needed)
+ * Logits should be finite: NaN logits are never selected, and a slot left without
+ * a candidate gets id -1 (which the expert calls skip).  Two kernel launches on
+ * hip_stream, deterministic.
+ * Returns MOE_OK, MOE_E_INVAL / MOE_E_DTYPE / MOE_E_WORKSPACE for bad arguments
+ * (nothing enqueued), or MOE_E_HIP.
+ */
+int moe_router_topk(const moe_layer_desc* desc, const void* w_router, const void* x, int32_t n,
+                    float* logits, int32_t* ids, float* w, void* ws, size_t ws_bytes,
+                    void* hip_stream);
+
+/* Workspace bytes of moe_router_topk for passes of up to n tokens (the largest over
+ * 1..n), or 0 for invalid arguments. */
+size_t moe_router_workspace_bytes(const moe_layer_desc* desc, int32_t n);
+
 /* Number of kernel launches moe_expert_perslot / moe_expert_dedup enqueue per
  * call (moe_route_group is a separate, optional launch), or a negative status for
  * a bad kind. */

@@ -11,6 +11,10 @@ CPU-baseline leg may import this package.  It shares no code with the GPU librar
 * ``step_exact.py``: the step-time model, speedup condition, staircase, step
   points and reuse thresholds in exact rational arithmetic (Sections 3.1-3.4,
   Appendix B).
+* ``fits.py``: the fits on chosen ids (Eq. (4), Eq. (E.1)), the bandwidth error
+  and the Table 2 bounds (Sections 2, 3.5, 4; Appendix C).
+* ``router.py``: the router ahead of the expert operation (Section 1): top-m
+  logits, ties to the lower id, softmax over the selected.
 """
 from .ffn import (  # noqa: F401
     build, route_group, union_count, union_count_batch, bytes_requested, expert_apply,

@@ -15,5 +15,5 @@ Both the GPU path's tests and the CPU oracle's tests take their inputs from here
 from .lib import (  # noqa: F401
     mix64, key_of, normal_f64, normal_f32, normal_bf16, bf16_to_f32, f32_to_bf16,
 )
-from .layers import CONFIGS, LayerSpec, layer_spec, expert_weights, layer_weights, pass_x  # noqa: F401
+from .layers import CONFIGS, LayerSpec, layer_spec, expert_weights, layer_weights, pass_x, router_weights  # noqa: F401,E501
 from . import routing  # noqa: F401

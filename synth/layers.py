@@ -19,6 +19,7 @@ from . import lib
 
 TAG_GATE, TAG_UP, TAG_DOWN, TAG_X = 1, 2, 3, 4
 TAG_SHARED = 16  # shared expert s uses tags TAG_SHARED + 4*s + {1,2,3}
+TAG_ROUTER = 15
 
 
 @dataclass(frozen=True)
@@ -101,3 +102,12 @@ def pass_x(spec, seed, layer, pass_id, n):
     if spec.dtype == "bf16":
         return lib.normal_bf16(k, n * spec.d, 1.0).reshape(n, spec.d)
     return lib.normal_f32(k, n * spec.d, 1.0).reshape(n, spec.d)
+
+
+def router_weights(spec, seed, layer=0, sigma=None):
+    """Router W_r [N][d] (bf16 bit patterns or fp32), sigma * N(0, 1) per element.
+    The default sigma makes the logits of N(0, 1) activations unit-variance
+    (sigma = 1/sqrt(d)), so that top-m selections have realistic margins."""
+    sg = (1.0 / np.sqrt(spec.d)) if sigma is None else sigma
+    blk = lib.blocks([lib.key_of(seed, layer, TAG_ROUTER, 0)], spec.N * spec.d, sg, spec.dtype)
+    return blk.reshape(spec.N, spec.d)

@@ -232,3 +232,27 @@ def test_step_time_model_rejects_bad_input():
         efa.step_time_model(2, [0.5], 1.0, E=[[1, 2], [1, 2]], beta=[[1, 0], [1, 1]])
     with pytest.raises(efa.MoeError):
         efa.step_time_model(2, [1.5], 1.0, E=[[1, 2], [1, 2]], beta=[[1, 1], [1, 1]])
+
+
+def test_router_host_validation():
+    L = _abi.lib()
+    vp = ctypes.c_void_p
+    fake = vp(0x1000)
+    assert L.moe_router_workspace_bytes(ctypes.byref(_desc(N=64, m=6, d_model=2048, dtype=_abi.MOE_BF16)), 8) == (
+        4 * 8 * 64 * 4)
+    d = _desc(N=512, m=8, d_model=2048, dtype=_abi.MOE_BF16)
+    need = L.moe_router_workspace_bytes(ctypes.byref(d), 8)
+    # 32 expert blocks x 1 token block: 4 parts of the contraction (the most)
+    assert need == 4 * 8 * 512 * 4
+    assert L.moe_router_workspace_bytes(ctypes.byref(_desc(N=64, m=65)), 8) == 0
+    assert L.moe_router_topk(ctypes.byref(_desc(N=64, m=6)), fake, fake, 8, fake, fake, fake, fake, 255,
+                             None) == _abi.MOE_E_WORKSPACE
+    assert L.moe_router_topk(ctypes.byref(_desc(N=64, m=6)), fake, fake, 8, fake, fake, fake, None, 1 << 20,
+                             None) == _abi.MOE_E_INVAL
+    assert L.moe_router_workspace_bytes(ctypes.byref(d), 65) == 0
+    args = lambda dd, n, ws_bytes: (ctypes.byref(dd), fake, fake, n, fake, fake, fake, fake, ws_bytes, None)
+    assert L.moe_router_topk(*args(d, 8, need - 1)) == _abi.MOE_E_WORKSPACE
+    assert L.moe_router_topk(*args(_desc(N=64, m=65), 8, need)) == _abi.MOE_E_INVAL
+    assert L.moe_router_topk(*args(_desc(d_model=60), 8, need)) == _abi.MOE_E_DTYPE
+    assert L.moe_router_topk(ctypes.byref(d), vp(0x1004), fake, 8, fake, fake, fake, fake, need,
+                             None) == _abi.MOE_E_INVAL
