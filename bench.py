@@ -378,7 +378,52 @@ def strip_bytes(rows):
     return [{k: v for k, v in r.items() if not k.startswith("bytes_")} for r in rows]
 
 
-def extra_configs(args, torch, efa, synth, routing, ev, flush, stream):
+def tree_selection(args, efa, routing, spec, layer, x, y, ws, timed, w_exp, ntrees, dedup_fit):
+    """The verification subtree of each seeded 32-node tree chosen by reward over
+    predicted cycle time (SpecFit Eq. (5), moe_tree_select, K = 7), with the cycle time
+    calibrated from the deduplicating kernel's fit on chosen ids (beta = c_g w per
+    union expert, b_k = t_op + c_t (k + 1)); the selected tokens are then run through
+    the dedup kernel and timed, next to the 7 nodes of highest cumulative
+    probability (the plain rule for a 7-node budget)."""
+    import torch
+    if dedup_fit is None:
+        return None
+    t_op, c_g, c_t = dedup_fit
+    K = 7
+    beta = c_g * w_exp
+    b = [max(t_op + c_t * (k + 1), 1e-9) for k in range(K + 1)]
+    rows = []
+    for i in range(1, ntrees + 1):
+        parent, ttr = routing.tree_routing(spec.N, spec.m, 0.5, routing.rng_for(args.seed, 0, "tree", i))
+        p = routing.tree_commit_probs(parent, routing.rng_for(args.seed, 0, "tree", 1000 + i))
+        bm = efa.expert_bitmaps(ttr.ids[:, None, :], spec.N)
+        s = efa.tree_select(parent, p, bm, K, b, beta)
+        top = sorted(range(1, 32), key=lambda v: (-p[v], v))[:K]
+        res = {}
+        for name, nodes in (("selected", [0] + s["ids"]), ("top7", [0] + sorted(top))):
+            ids = torch.from_numpy(np.ascontiguousarray(ttr.ids[nodes])).cuda()
+            w = torch.from_numpy(np.ascontiguousarray(ttr.w[nodes])).cuda()
+            n = len(nodes)
+            t = float(np.median([timed(lambda: efa.expert_dedup(layer, x[:n], ids, w, y=y[:n], ws=ws))
+                                 for _ in range(3)])) * 1e-3
+            R = 1.0 + float(sum(p[v] for v in nodes[1:]))
+            U = len(set(ttr.ids[nodes].reshape(-1).tolist()))
+            res[name] = dict(nodes=n - 1, R=R, U=U, t_meas=t, t_pred=b[n - 1] + beta * U)
+        rows.append(res)
+    def mean(k, f):
+        return float(np.mean([r[k][f] for r in rows]))
+    out = {"workload": "%d seeded 32-node trees, commit probabilities per tree, K = 7, one qwen3-shaped layer"
+                       % ntrees, "beta_us_per_union_expert": beta * 1e6, "b_us": [v * 1e6 for v in b]}
+    for k in ("selected", "top7"):
+        out[k] = {"nodes": mean(k, "nodes"), "R": mean(k, "R"), "U": mean(k, "U"),
+                  "t_meas_us": mean(k, "t_meas") * 1e6, "t_pred_us": mean(k, "t_pred") * 1e6,
+                  "R_per_ms_measured": float(np.mean([r[k]["R"] / r[k]["t_meas"] for r in rows])) * 1e-3,
+                  "pred_rel_err_median": float(np.median([abs(r[k]["t_pred"] - r[k]["t_meas"]) / r[k]["t_meas"]
+                                                          for r in rows]))}
+    return out
+
+
+def extra_configs(args, torch, efa, synth, routing, ev, flush, stream, dedup_fit=None):
     """The other workloads: the Qwen3-30B-A3B-shaped layer 48 times back to back per
     pass (zipf routing), the 32-node draft tree on that layer, and the
     Mixtral-8x7B-shaped layer (uniform and repeat-0.6 routing).  Weights from the
@@ -460,10 +505,11 @@ def extra_configs(args, torch, efa, synth, routing, ev, flush, stream):
             trecs.append(dict(n=32, U=U, bytes_slot=32 * spec.m * w_exp, bytes_dedup=U * w_exp, t_slot_ms=ts,
                               t_dedup_ms=td))
     trow = per_n_rows(trecs, [32])[0]
+    sel = tree_selection(args, efa, routing, spec, tl, x, y, ws32, timed, w_exp, ntrees, dedup_fit)
     out["tree"] = {"workload": "32-node ancestor-closed draft tree (1+1+2+4+8+16, children reuse parent experts "
                                "with p=0.5) on one qwen3-shaped layer, %d seeded trees" % ntrees,
                    **{k: v for k, v in trow.items() if not k.startswith("bytes_")},
-                   "bytes_slot": trow["bytes_slot"], "bytes_dedup_mean": trow["bytes_dedup"]}
+                   "bytes_slot": trow["bytes_slot"], "bytes_dedup_mean": trow["bytes_dedup"], "selection": sel}
     del layers, tl
     torch.cuda.empty_cache()
 
@@ -724,7 +770,10 @@ def main():
     if not args.no_extras and args.config == "dsv2lite":
         del passes, layer
         torch.cuda.empty_cache()
-        extras.update(extra_configs(args, torch, efa, synth, routing, ev, flush, stream))
+        fit = extras.get("chosen_ids", {}).get("fit_dedup")
+        dfit = None if fit is None else (fit["t_op_us"] * 1e-6, fit["c_g_s_per_GB"] * 1e-9,
+                                         fit["c_t_us_per_token"] * 1e-6)
+        extras.update(extra_configs(args, torch, efa, synth, routing, ev, flush, stream, dedup_fit=dfit))
 
     out = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,

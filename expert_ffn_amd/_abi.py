@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_E_INVAL", -2: "MOE_E_DTYPE", -3: "MOE_E_WO
 EXPORTS = ("moe_route_group", "moe_workspace_bytes", "moe_expert_perslot", "moe_expert_dedup",
            "moe_kernels_per_call", "moe_expert_perslot_ev", "moe_expert_dedup_ev", "bytes_requested",
            "step_time_model", "moe_pack_w_down", "moe_fit_times", "moe_error_bounds",
-           "moe_router_topk", "moe_router_workspace_bytes")
+           "moe_router_topk", "moe_router_workspace_bytes", "moe_tree_select")
 
 
 class MoeError(RuntimeError):
@@ -44,6 +44,21 @@ class LayerWeights(ctypes.Structure):
     _fields_ = [("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
                 ("w_gate_shared", ctypes.c_void_p), ("w_up_shared", ctypes.c_void_p),
                 ("w_down_shared", ctypes.c_void_p)]
+
+
+MOE_TREE_MAXV, MOE_TREE_MAXK, MOE_TREE_MAXW = 63, 16, 16
+
+
+class TreeIn(ctypes.Structure):
+    _fields_ = [("V", ctypes.c_int32), ("L", ctypes.c_int32), ("words", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("parent", ctypes.c_void_p), ("p", ctypes.c_void_p), ("bitmap", ctypes.c_void_p),
+                ("b", ctypes.c_void_p), ("beta", ctypes.c_double), ("max_level", ctypes.c_int32),
+                ("level", ctypes.c_void_p)]
+
+
+class TreeOut(ctypes.Structure):
+    _fields_ = [("selected", ctypes.c_uint64), ("count", ctypes.c_int32), ("F", ctypes.c_int32),
+                ("R", ctypes.c_double), ("T", ctypes.c_double), ("visited", ctypes.c_int64)]
 
 
 _NM, _AM = MOE_STEP_NMAX, MOE_STEP_AMAX
@@ -110,6 +125,8 @@ def lib():
             L.moe_router_topk.restype = ctypes.c_int
             L.moe_router_workspace_bytes.argtypes = [pdesc, ctypes.c_int32]
             L.moe_router_workspace_bytes.restype = sz
+            L.moe_tree_select.argtypes = [ctypes.POINTER(TreeIn), ctypes.POINTER(TreeOut)]
+            L.moe_tree_select.restype = ctypes.c_int
             _LIB = L
     return _LIB
 

@@ -8,6 +8,8 @@
 //   Section 2 Eq. (4) and Appendix E Eq. (E.1): least-squares fits of the kernels'
 //   times over passes with chosen ids.  Section 3.5, Table 2 and Appendix C: the
 //   error bounds for a relative bandwidth error eps.
+// SpecFit, arXiv:2610.15417, Sections 3.1-3.3 and Algorithm 1: the exact search for
+// the verification subtree with the largest reward over predicted cycle time.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -233,6 +235,116 @@ int moe_error_bounds(double eps, double* out) {
     out[2] = delta;                                // from eps to delta
     out[3] = (1.0 - delta) / (1.0 + delta);        // (20)
     out[4] = (1.0 + delta) / (1.0 - delta);        // (21)
+    return MOE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+struct TreeSearch {
+    const moe_tree_in* in;
+    int V, L, W;
+    std::vector<uint64_t> stack;  // per depth: L * W words of the carried unions
+    int ids[MOE_TREE_MAXK];       // current subset, increasing ids
+    // incumbent
+    double bR, bT;
+    int bF, bn;
+    int bids[MOE_TREE_MAXK];
+    int64_t visited;
+
+    bool usable(int v) const { return in->max_level <= 0 || in->level[v] <= in->max_level; }
+
+    // candidate (R, T, F, n, ids) against the incumbent: ratio, then R, then -F, then
+    // -n; otherwise the earlier subset in enumeration order (the lexicographically
+    // smaller id list) stays
+    void offer(double R, double T, int F, int n) {
+        ++visited;
+        const double lhs = R * bT, rhs = bR * T;  // R/T vs bR/bT, T > 0
+        bool better = lhs > rhs;
+        if (lhs == rhs) {
+            if (R != bR) better = R > bR;
+            else if (F != bF) better = F < bF;
+            else better = n < bn;
+        }
+        if (better) {
+            bR = R;
+            bT = T;
+            bF = F;
+            bn = n;
+            for (int i = 0; i < n; ++i) bids[i] = ids[i];
+        }
+    }
+
+    int popcount_state(const uint64_t* st) const {
+        int f = 0;
+        for (int i = 0; i < L * W; ++i) f += __builtin_popcountll(st[i]);
+        return f;
+    }
+
+    // S = ids[0..n) with unions in stack[n]; extend by every later eligible node
+    void dfs(int n, int last, double R, const std::vector<char>& in_s) {
+        if (n == in->K) return;
+        std::vector<char> mark(in_s);
+        for (int v = last + 1; v <= V; ++v) {
+            if (!usable(v)) continue;
+            const int pa = in->parent[v];
+            if (pa != 0 && !mark[pa]) continue;
+            const uint64_t* cur = &stack[(size_t)n * L * W];
+            uint64_t* nxt = &stack[(size_t)(n + 1) * L * W];
+            const uint64_t* bv = in->bitmap + (size_t)v * L * W;
+            for (int i = 0; i < L * W; ++i) nxt[i] = cur[i] | bv[i];
+            ids[n] = v;
+            const double Rv = R + in->p[v];
+            const int F = popcount_state(nxt);
+            offer(Rv, in->b[n + 1] + in->beta * F, F, n + 1);
+            mark[v] = 1;
+            dfs(n + 1, v, Rv, mark);
+            mark[v] = 0;
+        }
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+int moe_tree_select(const moe_tree_in* in, moe_tree_out* out) {
+    if (!in || !out || !in->parent || !in->p || !in->bitmap || !in->b) return MOE_E_INVAL;
+    if (in->V < 0 || in->V > MOE_TREE_MAXV || in->L < 1 || in->words < 1 || in->words > MOE_TREE_MAXW ||
+        in->K < 0 || in->K > MOE_TREE_MAXK)
+        return MOE_E_INVAL;
+    if (!(in->beta > 0.0) || !isfinite(in->beta)) return MOE_E_INVAL;
+    if (in->max_level > 0 && !in->level) return MOE_E_INVAL;
+    for (int k = 0; k <= in->K; ++k)
+        if (!(in->b[k] > 0.0) || !isfinite(in->b[k])) return MOE_E_INVAL;
+    for (int v = 1; v <= in->V; ++v) {
+        if (in->parent[v] < 0 || in->parent[v] >= v) return MOE_E_INVAL;
+        if (!(in->p[v] >= 0.0) || !isfinite(in->p[v])) return MOE_E_INVAL;
+    }
+    TreeSearch ts;
+    ts.in = in;
+    ts.V = in->V;
+    ts.L = in->L;
+    ts.W = in->words;
+    ts.stack.assign((size_t)(in->K + 1) * in->L * in->words, 0ull);
+    for (int i = 0; i < in->L * in->words; ++i) ts.stack[i] = in->bitmap[i];  // the root's experts
+    ts.visited = 0;
+    const int F0 = ts.popcount_state(ts.stack.data());
+    ts.bR = 1.0;
+    ts.bT = in->b[0] + in->beta * F0;
+    ts.bF = F0;
+    ts.bn = 0;
+    ts.visited = 1;
+    std::vector<char> mark((size_t)in->V + 1, 0);
+    ts.dfs(0, 0, 1.0, mark);
+    out->selected = 0;
+    for (int i = 0; i < ts.bn; ++i) out->selected |= 1ull << (ts.bids[i] - 1);
+    out->count = ts.bn;
+    out->F = ts.bF;
+    out->R = ts.bR;
+    out->T = ts.bT;
+    out->visited = ts.visited;
     return MOE_OK;
 }
 

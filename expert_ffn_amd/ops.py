@@ -288,3 +288,35 @@ def error_bounds(eps):
     check("moe_error_bounds", lib().moe_error_bounds(float(eps), out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
     return {"time_factor": float(out[0]), "faster_margin": float(out[1]), "delta": float(out[2]),
             "regret_factor": float(out[3]), "speedup_factor": float(out[4])}
+
+
+def expert_bitmaps(ids, N):
+    """Per node and layer the bitmap of its experts: ids int [V+1][L][m] -> uint64
+    [V+1][L][ceil(N/64)] (argument marshalling for ``tree_select``)."""
+    ids = np.asarray(ids, dtype=np.int64)
+    W = (int(N) + 63) // 64
+    out = np.zeros(ids.shape[:2] + (W,), np.uint64)
+    for v in range(ids.shape[0]):
+        for l in range(ids.shape[1]):
+            for e in ids[v, l]:
+                out[v, l, e // 64] |= np.uint64(1) << np.uint64(e % 64)
+    return out
+
+
+def tree_select(parent, p, bitmaps, K, b, beta, max_level=0, level=None):
+    """The verification subtree with the largest reward over predicted cycle time
+    (``moe_tree_select``).  Returns a dict: ids (sorted node ids), R, T, F, visited."""
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    bm = np.ascontiguousarray(bitmaps, dtype=np.uint64)
+    b = np.ascontiguousarray(b, dtype=np.float64)
+    V = parent.size - 1
+    if bm.ndim != 3 or bm.shape[0] != V + 1 or p.size != V + 1 or b.size != int(K) + 1:
+        raise ValueError("shapes: parent/p [V+1], bitmaps [V+1][L][words], b [K+1]")
+    lv = None if level is None else np.ascontiguousarray(level, dtype=np.int32)
+    ti = _abi.TreeIn(V, bm.shape[1], bm.shape[2], int(K), parent.ctypes.data, p.ctypes.data, bm.ctypes.data,
+                     b.ctypes.data, float(beta), int(max_level), None if lv is None else lv.ctypes.data)
+    to = _abi.TreeOut()
+    check("moe_tree_select", lib().moe_tree_select(ctypes.byref(ti), ctypes.byref(to)))
+    ids = [v + 1 for v in range(64) if (to.selected >> v) & 1]
+    return {"ids": ids, "R": to.R, "T": to.T, "F": to.F, "visited": to.visited}

@@ -336,6 +336,52 @@ int moe_fit_times(int32_t kind, int32_t count, const int32_t* n, const int32_t* 
  */
 int moe_error_bounds(double eps, double* out);
 
+/* ---------------------------------------------------------------------------
+ * moe_tree_select -- the verification subtree of a draft tree chosen by reward over
+ * predicted cycle time (SpecFit, arXiv:2610.15417, Sections 3.1-3.3, Algorithm 1),
+ * host only.  Node 0 is the root s (the current token), nodes 1..V the draft pool,
+ * parent[v] < v (parents before descendants; parent[v] = 0 for children of the root).
+ *   legal family: S ancestor-closed (v in S => parent[v] in S or is the root), |S| <= K
+ *   R(S) = 1 + sum_{v in S} p[v]
+ *   F(S) = sum over layers l of |E_l(root) u U_{v in S} E_l(v)|   (expert bitmaps, popcount)
+ *   T(S) = b[|S|] + beta F(S)
+ * The selection maximises R/T; equal ratios prefer the larger R, the smaller F, fewer
+ * nodes, then the lexicographically smaller list of node ids.  The search is the
+ * depth-first enumeration that adds nodes in increasing id order, each only when its
+ * parent is present, carrying the per-layer unions as bitmaps; ratios are compared by
+ * cross-multiplication.  With max_level > 0 only nodes with level[v] <= max_level take
+ * part (the selection after drafting max_level levels, Appendix A.2).
+ * Used here with T calibrated from the deduplicating kernel's measured cost per union
+ * expert and per pass (beta = c_g w, b_k from t_op + c_t (k+1)), in place of SpecFit's
+ * host-to-device transfer cost.
+ * Returns MOE_OK, or MOE_E_INVAL for sizes out of range, a bad parent, b or beta not
+ * positive, or p negative.
+ */
+#define MOE_TREE_MAXV 63   /* draft nodes */
+#define MOE_TREE_MAXK 16   /* largest subtree */
+#define MOE_TREE_MAXW 16   /* 64-bit words of one layer's expert bitmap (N <= 1024) */
+typedef struct {
+    int32_t V;               /* draft nodes 1..V */
+    int32_t L;               /* layers */
+    int32_t words;           /* 64-bit words per layer bitmap, 1..MOE_TREE_MAXW */
+    int32_t K;               /* largest subtree, 0..MOE_TREE_MAXK */
+    const int32_t* parent;   /* [V+1]; parent[0] ignored */
+    const double* p;         /* [V+1]; commit probability of node v; p[0] ignored */
+    const uint64_t* bitmap;  /* [(V+1)][L][words]: bit e of layer l of node v = expert e */
+    const double* b;         /* [K+1] intercepts, > 0 */
+    double beta;             /* cost per union expert, > 0 */
+    int32_t max_level;       /* <= 0: every node */
+    const int32_t* level;    /* [V+1] depth of each node (root 0), read when max_level > 0 */
+} moe_tree_in;
+typedef struct {
+    uint64_t selected;       /* bit v-1 set for each selected node v */
+    int32_t count;           /* |S| */
+    int32_t F;               /* union feature of S */
+    double R, T;             /* reward and predicted cycle time of S */
+    int64_t visited;         /* legal subtrees enumerated (the root-only one included) */
+} moe_tree_out;
+int moe_tree_select(const moe_tree_in* in, moe_tree_out* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,6 +18,10 @@ Readings used where the workload descriptions leave a step open:
   child, every node at depths 1..4 with two children; node ids breadth first
   (parents before children); node 0 uniform, every other node drawn from its
   parent by the ``correlated`` rule;
+* tree commit probabilities (for choosing a verification subtree): node v's
+  cumulative draft probability is its parent's times a conditional one; the root's
+  single child draws U(0.5, 0.95), a first child U(0.4, 0.9) and a second child
+  U(0, 1 - q_first) / 2, so probabilities fall along every path;
 * ``chosen`` (passes with chosen ids): the n m slots of a pass name exactly U
   distinct experts, m <= U <= min(n m, N), a seeded U-subset of the N; token 0
   takes m of them, the other U - m are spread as evenly as possible over tokens
@@ -112,6 +116,24 @@ def tree_routing(N, m, p, rng):
     logits = rng.standard_normal((parents.size, m))
     tr = _finish(rows, logits)
     return parents, tr
+
+
+def tree_commit_probs(parents, rng):
+    """Cumulative draft probability of every node (root: 1)."""
+    parents = np.asarray(parents)
+    p = np.ones(parents.size, np.float64)
+    first = {}
+    for v in range(1, parents.size):
+        pa = int(parents[v])
+        if pa == 0 and v == 1:
+            q = rng.uniform(0.5, 0.95)
+        elif pa not in first:
+            q = rng.uniform(0.4, 0.9)
+            first[pa] = q
+        else:
+            q = rng.uniform(0.0, 1.0 - first[pa]) / 2
+        p[v] = p[pa] * q
+    return p
 
 
 def chosen_pass(N, m, n, U, rng):
