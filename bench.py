@@ -213,6 +213,41 @@ def write_profile_summary(prof_dir, bench_json, config):
     print(path)
 
 
+def dispatch_section(args, efa, layer, ws, ys, passes, kinds, nvals, per_kind, flush, ev, stream):
+    """The crossover-driven switch (moe_expert_auto) on held-out windows: the crossover
+    comes from the timed windows' measured S(n); the warm-up windows, never used for
+    it, are run by both kernels and by the switch, each after the flush."""
+    e2 = ev.make(2)
+    out = {"workload": "warm-up windows of each routing (not used for the crossover), n = 1..%d" % nvals[-1]}
+    held = [s_ for s_ in range(args.warmup)] or [0]
+    for kind, _ in kinds:
+        c = int(per_kind[kind]["crossover"])
+        tot = {"slot": 0.0, "dedup": 0.0, "auto": 0.0, "best": 0.0}
+        for n in nvals:
+            for s_ in held:
+                p = passes[(kind, n, s_)]
+                t = {}
+                for name, call in (("slot", lambda: efa.expert_perslot(layer, p["x"], p["ids"], p["w"], y=ys[n], ws=ws,
+                                                                       stream=stream)),
+                                   ("dedup", lambda: efa.expert_dedup(layer, p["x"], p["ids"], p["w"], y=ys[n], ws=ws,
+                                                                      stream=stream)),
+                                   ("auto", lambda: efa.expert_auto(layer, p["x"], p["ids"], p["w"], c, y=ys[n], ws=ws,
+                                                                    stream=stream))):
+                    flush()
+                    ev.record(e2[0], stream.cuda_stream)
+                    call()
+                    ev.record(e2[1], stream.cuda_stream)
+                    t[name] = ev.ms(e2[0], e2[1]) * 1e3
+                for k in ("slot", "dedup", "auto"):
+                    tot[k] += t[k]
+                tot["best"] += min(t["slot"], t["dedup"])
+        out[kind] = {"crossover": c, **{k + "_us_total": round(v, 1) for k, v in tot.items()},
+                     "auto_over_best": round(tot["auto"] / tot["best"], 4),
+                     "auto_over_slot": round(tot["auto"] / tot["slot"], 4),
+                     "auto_over_dedup": round(tot["auto"] / tot["dedup"], 4)}
+    return out
+
+
 def router_section(args, efa, synth, spec, passes, kinds, nvals, flush, ev, stream):
     """The router ahead of the expert operation (two launches: logits, then top-m and
     softmax) on the layer's own activations, after the flush, events around both."""
@@ -754,6 +789,8 @@ def main():
     if not args.no_extras and args.config == "dsv2lite":
         ws9 = layer.workspace(9)
         extras["router"] = router_section(args, efa, synth, spec, passes, kinds, nvals, flush, ev, stream)
+        extras["dispatch"] = dispatch_section(args, efa, layer, ws, ys, passes, kinds, nvals, per_kind, flush, ev,
+                                              stream)
         extras["chosen_ids"] = chosen_id_section(
             args, efa, routing, spec, layer, ws9, ys, flush, ev, stream, recs, per_kind,
             lambda n: to_torch(synth.pass_x(spec, args.seed, 0, 77000 + n, n)))

@@ -9,6 +9,6 @@ from ._abi import (  # noqa: F401
     MOE_KIND_DEDUP, MOE_KIND_SLOT, MoeError, lib,
 )
 from .ops import (  # noqa: F401
-    Grouping, Layer, bytes_requested, error_bounds, expert_bitmaps, expert_dedup, expert_perslot, fit_times,
+    Grouping, Layer, bytes_requested, error_bounds, expert_auto, expert_bitmaps, expert_dedup, expert_perslot, fit_times,
     kernels_per_call, pack_w_down, route_group, router_topk, step_time_model, tree_select,
 )

@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_E_INVAL", -2: "MOE_E_DTYPE", -3: "MOE_E_WO
 EXPORTS = ("moe_route_group", "moe_workspace_bytes", "moe_expert_perslot", "moe_expert_dedup",
            "moe_kernels_per_call", "moe_expert_perslot_ev", "moe_expert_dedup_ev", "bytes_requested",
            "step_time_model", "moe_pack_w_down", "moe_fit_times", "moe_error_bounds",
-           "moe_router_topk", "moe_router_workspace_bytes", "moe_tree_select")
+           "moe_router_topk", "moe_router_workspace_bytes", "moe_tree_select",
+           "moe_expert_auto")
 
 
 class MoeError(RuntimeError):
@@ -127,6 +128,8 @@ def lib():
             L.moe_router_workspace_bytes.restype = sz
             L.moe_tree_select.argtypes = [ctypes.POINTER(TreeIn), ctypes.POINTER(TreeOut)]
             L.moe_tree_select.restype = ctypes.c_int
+            L.moe_expert_auto.argtypes = [pdesc, pw, vp, vp, vp, i32, vp, vp, vp, sz, i32, vp, vp]
+            L.moe_expert_auto.restype = ctypes.c_int
             _LIB = L
     return _LIB
 

@@ -1531,6 +1531,18 @@ int moe_expert_dedup(const moe_layer_desc* desc, const moe_layer_weights* weight
     return run_expert<kDedup>(desc, weights, x, ids, w, n, y, info, ws, ws_bytes, hip_stream, nullptr, 0);
 }
 
+int moe_expert_auto(const moe_layer_desc* desc, const moe_layer_weights* weights, const void* x, const int32_t* ids,
+                    const float* w, int32_t n, float* y, int32_t* info, void* ws, size_t ws_bytes, int32_t crossover,
+                    int32_t* kind_out, void* hip_stream) {
+    if (crossover < 0) return MOE_E_INVAL;
+    const bool dedup = crossover > 0 && n >= crossover;
+    const int rc = dedup ? run_expert<kDedup>(desc, weights, x, ids, w, n, y, info, ws, ws_bytes, hip_stream, nullptr, 0)
+                         : run_expert<kPerSlot>(desc, weights, x, ids, w, n, y, info, ws, ws_bytes, hip_stream, nullptr,
+                                                0);
+    if (rc == MOE_OK && kind_out) *kind_out = dedup ? MOE_KIND_DEDUP : MOE_KIND_SLOT;
+    return rc;
+}
+
 int moe_expert_perslot_ev(const moe_layer_desc* desc, const moe_layer_weights* weights, const void* x,
                           const int32_t* ids, const float* w, int32_t n, float* y, int32_t* info, void* ws,
                           size_t ws_bytes, void* hip_stream, void* const* events, int32_t n_events) {

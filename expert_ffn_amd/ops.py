@@ -215,6 +215,21 @@ def expert_dedup(layer, x, ids, w, y=None, ws=None, info=None, accumulate=False,
                 events, MOE_KIND_DEDUP, "moe_expert_dedup")
 
 
+def expert_auto(layer, x, ids, w, crossover, y=None, ws=None, info=None, accumulate=False, stream=None):
+    """The crossover-driven switch (``moe_expert_auto``): the deduplicating kernel from
+    n >= crossover tokens, the per-slot kernel below (crossover 0: always per-slot).
+    Returns (y, kind run)."""
+    n, y, ws = _prep(layer, x, ids, w, y, ws, MOE_KIND_DEDUP)
+    if info is not None:
+        _check_dev("info", info, torch.int32, (3,))
+    desc = layer.desc(accumulate)
+    kind = ctypes.c_int32(-1)
+    st = lib().moe_expert_auto(ctypes.byref(desc), ctypes.byref(layer._weights), _vp(x), _vp(ids), _vp(w), n, _vp(y),
+                               _vp(info), _vp(ws), ws.numel(), int(crossover), ctypes.byref(kind), _stream(stream))
+    check("moe_expert_auto", st)
+    return y, kind.value
+
+
 def kernels_per_call(kind):
     return lib().moe_kernels_per_call(int(kind))
 

@@ -168,6 +168,23 @@ int moe_expert_dedup(const moe_layer_desc* desc, const moe_layer_weights* weight
                      void* ws, size_t ws_bytes, void* hip_stream);
 
 /*
+ * moe_expert_auto -- the crossover-driven switch between the two kernels (paper
+ * Section 2 "Bytes against bandwidth" and Section 4: the deduplicating kernel should
+ * run from the pass size at which its saving S(n) stays positive): passes of
+ * n >= crossover tokens run moe_expert_dedup, smaller ones moe_expert_perslot;
+ * crossover = 0 (no crossover) always runs the per-slot kernel.  The crossover comes
+ * from measured times (step_time_model's crossover, or the measured S(n)).
+ * Arguments as for moe_expert_perslot; ws must serve the kernel that runs (a
+ * workspace of the larger of the two moe_workspace_bytes serves both).  kind_out
+ * (host, may be NULL) receives MOE_KIND_SLOT or MOE_KIND_DEDUP.  Returns what the
+ * chosen call returns, or MOE_E_INVAL for crossover < 0.
+ */
+int moe_expert_auto(const moe_layer_desc* desc, const moe_layer_weights* weights, const void* x,
+                    const int32_t* ids, const float* w, int32_t n, float* y, int32_t* info,
+                    void* ws, size_t ws_bytes, int32_t crossover, int32_t* kind_out,
+                    void* hip_stream);
+
+/*
  * moe_pack_w_down -- copy W_down [N][d_model][d_ff] into the packed layout
  * [N][d_ff/8][d_model][8]: element (e, i, f) goes to
  *     ((e*(d_ff/8) + f/8)*d_model + i)*8 + f%8,

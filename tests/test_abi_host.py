@@ -256,3 +256,15 @@ def test_router_host_validation():
     assert L.moe_router_topk(*args(_desc(d_model=60), 8, need)) == _abi.MOE_E_DTYPE
     assert L.moe_router_topk(ctypes.byref(d), vp(0x1004), fake, 8, fake, fake, fake, fake, need,
                              None) == _abi.MOE_E_INVAL
+
+
+def test_expert_auto_rejects_negative_crossover():
+    L = _abi.lib()
+    fake = ctypes.c_void_p(0x1000)
+    W = _abi.LayerWeights(0x1000, 0x1000, 0x1000)
+    d = _desc()
+    assert L.moe_expert_auto(ctypes.byref(d), ctypes.byref(W), fake, fake, fake, 4, fake, None, fake, 1 << 30, -1,
+                             None, None) == _abi.MOE_E_INVAL
+    # a bad descriptor is reported by the kernel it would run, before any launch
+    assert L.moe_expert_auto(ctypes.byref(_desc(m=0)), ctypes.byref(W), fake, fake, fake, 4, fake, None, fake,
+                             1 << 30, 2, None, None) == _abi.MOE_E_INVAL

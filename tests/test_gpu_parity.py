@@ -359,3 +359,24 @@ def test_repeated_ids_count_as_often_as_they_appear(packed):
     ref = oracle.moe_ffn(*dl.host, x, ids1, w1, "bf16")
     assert_close(ys, ref, "repeated ids perslot")
     assert_close(yd, ref, "repeated ids dedup")
+
+
+def test_expert_auto_runs_the_kernel_the_crossover_names():
+    """moe_expert_auto: the deduplicating kernel from n >= crossover, the per-slot
+    kernel below, crossover 0 always per-slot; same bits as the kernel called directly."""
+    spec = synth.layer_spec("dsv2lite", N=16, m=4, d=256, d_ff=176, n_shared=0)
+    dl = DeviceLayer(spec, 21, packed=True)
+    tr = routing.make_trace(spec, "correlated", 32, seed=21, p=0.5)
+    ws = dl.dev.workspace(8)
+    for n in (1, 2, 5):
+        ids_h, w_h = routing.window(tr, 4, n)
+        x = to_torch(synth.pass_x(spec, 21, 0, n, n))
+        ids, w = torch.from_numpy(ids_h).cuda(), torch.from_numpy(w_h).cuda()
+        ys = efa.expert_perslot(dl.dev, x, ids, w, ws=ws)
+        yd = efa.expert_dedup(dl.dev, x, ids, w, ws=ws)
+        for c in (0, 1, 3):
+            say("auto n", n, "crossover", c)
+            y, kind = efa.expert_auto(dl.dev, x, ids, w, c, ws=ws)
+            want = efa.MOE_KIND_DEDUP if (c > 0 and n >= c) else efa.MOE_KIND_SLOT
+            assert kind == want
+            assert torch.equal(y, yd if want == efa.MOE_KIND_DEDUP else ys)
