@@ -197,7 +197,8 @@ def write_profile_summary(prof_dir, bench_json, config):
     for k in sorted(d):
         v = d[k]
         lines.append("| `%s` | %d | %d | %.2f | %.2f | %.2f |" % (k[0], k[1], len(v), sum(v) / len(v), min(v), max(v)))
-    slot = [v for k, vs in d.items() if k[0].startswith("k_expert<true, 0") for v in vs]
+    # the per-slot bf16 kernel without shared experts (the last template flag), as timed
+    slot = [v for k, vs in d.items() if k[0].startswith("k_expert<true, 0") and k[0].endswith("false>") for v in vs]
     rf = b["roofline"]
     lines += ["", "## Bench line of the same run (HIP events on the launch stream)", "",
               "- value: %.1f GB/s (all passes, both kernels)" % b["value"],
