@@ -68,6 +68,18 @@ class HipEvents:
         return float(f.value)
 
 
+WEIGHT_LAYOUT = "tiled"  # moe_pack_tiled: 16-row x 64-byte blocks, waves on interleaved K steps
+
+
+def load_layout(layer):
+    """The layer in the layout the timed runs use: all three matrices tiled when
+    d and d_ff are whole 64-byte steps, else W_down packed."""
+    step = 32 if layer.dtype.itemsize == 2 else 16
+    if layer.d % step == 0 and layer.d_ff % step == 0:
+        return layer.tiled_copy()
+    return layer.packed_copy()
+
+
 def source_hash():
     h = hashlib.sha256()
     for p in ("expert_ffn_amd/csrc/moe_expert.hip",):
@@ -484,7 +496,7 @@ def extra_configs(args, torch, efa, synth, routing, ev, flush, stream, dedup_fit
     # ---- Qwen3-shaped: 48 layers back to back ----
     spec = synth.CONFIGS["qwen3"]
     L = spec.layers
-    layers = [efa.Layer(*device_layer_weights(spec, args.seed, l), m=spec.m).packed_copy() for l in range(L)]
+    layers = [load_layout(efa.Layer(*device_layer_weights(spec, args.seed, l), m=spec.m)) for l in range(L)]
     T = 1024
     traces = [routing.make_trace(spec, "zipf", T, seed=args.seed, layer=l, s=1.1) for l in range(L)]
     ws = layers[0].workspace(8)
@@ -551,7 +563,7 @@ def extra_configs(args, torch, efa, synth, routing, ev, flush, stream, dedup_fit
 
     # ---- Mixtral-shaped ----
     spec = synth.CONFIGS["mixtral"]
-    ml = efa.Layer(*device_layer_weights(spec, args.seed, 0), m=spec.m).packed_copy()
+    ml = load_layout(efa.Layer(*device_layer_weights(spec, args.seed, 0), m=spec.m))
     wsm = ml.workspace(8)
     w_exp = spec.expert_bytes
     mix = {}
@@ -626,8 +638,8 @@ def main():
     T = 4096
     t_setup = time.perf_counter()
     host_w = synth.layer_weights(spec, args.seed)
-    # W_down in the packed layout (moe_pack_w_down), done once at weight-load time
-    layer = efa.Layer(*(to_torch(a) for a in host_w), m=spec.m).packed_copy()
+    # weights in the tiled layout (moe_pack_tiled), done once at weight-load time
+    layer = load_layout(efa.Layer(*(to_torch(a) for a in host_w), m=spec.m))
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     nsteps_total = args.warmup + args.steps
@@ -717,7 +729,7 @@ def main():
     shared_us = []
     if spec.n_shared:
         sh_host = synth.layer_weights(spec, args.seed, shared=True)
-        shl = efa.Layer(*(to_torch(a) for a in sh_host), m=spec.n_shared).packed_copy()
+        shl = load_layout(efa.Layer(*(to_torch(a) for a in sh_host), m=spec.n_shared))
         sws = shl.workspace(nvals[-1])
         e2 = ev.make(2)
         for n in nvals:
@@ -732,7 +744,7 @@ def main():
             shared_us.append(sorted(tl[1:])[1])
         # the same experts computed in the routed call itself (one launch): routed
         # alone and routed + shared on the same windows, paired, both kernels
-        fl = efa.Layer(layer.w_gate, layer.w_up, layer.w_down, m=spec.m, packed=layer.packed,
+        fl = efa.Layer(layer.w_gate, layer.w_up, layer.w_down, m=spec.m, packed=layer.packed, tiled=layer.tiled,
                        shared=(shl.w_gate, shl.w_up, shl.w_down))
         fws = fl.workspace(nvals[-1])
         fused = {"routed_slot": [], "fused_slot": [], "routed_dedup": [], "fused_dedup": []}
@@ -818,7 +830,7 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "%s-shaped MoE layer expert op, n=1..%d, routing %s" % (
                args.config, nvals[-1], "+".join(k for k, _ in kinds)),
-               "N": spec.N, "m": spec.m, "d_model": spec.d, "d_ff": spec.d_ff, "w_down_layout": "packed",
+               "N": spec.N, "m": spec.m, "d_model": spec.d, "d_ff": spec.d_ff, "weight_layout": WEIGHT_LAYOUT,
                "passes_per_step": len(kinds) * len(nvals) * 2,
                "scrub_bytes": 0 if args.no_scrub else SCRUB_BYTES},
            "roofline": roofline, "cpu_baseline": cpu, "results": per_kind, "extras": extras,

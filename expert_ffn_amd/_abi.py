@@ -16,6 +16,8 @@ MOE_KIND_SLOT, MOE_KIND_DEDUP = 0, 1
 MOE_MAX_SLOTS, MOE_MAX_TOKENS, MOE_MAX_EXPERTS, MOE_MAX_SHARED = 256, 64, 1024, 16
 MOE_FLAG_ACCUMULATE = 1
 MOE_FLAG_WDOWN_PACKED = 2
+MOE_FLAG_TILED = 4
+MOE_MAT_GATE_UP, MOE_MAT_DOWN = 0, 1
 MOE_STEP_NMAX, MOE_STEP_AMAX = 16, 64
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_E_INVAL", -2: "MOE_E_DTYPE", -3: "MOE_E_WORKSPACE",
@@ -26,7 +28,7 @@ EXPORTS = ("moe_route_group", "moe_workspace_bytes", "moe_expert_perslot", "moe_
            "moe_kernels_per_call", "moe_expert_perslot_ev", "moe_expert_dedup_ev", "bytes_requested",
            "step_time_model", "moe_pack_w_down", "moe_fit_times", "moe_error_bounds",
            "moe_router_topk", "moe_router_workspace_bytes", "moe_tree_select",
-           "moe_expert_auto")
+           "moe_expert_auto", "moe_pack_tiled")
 
 
 class MoeError(RuntimeError):
@@ -116,6 +118,8 @@ def lib():
             L.step_time_model.restype = ctypes.c_int
             L.moe_pack_w_down.argtypes = [pdesc, vp, vp, vp]
             L.moe_pack_w_down.restype = ctypes.c_int
+            L.moe_pack_tiled.argtypes = [pdesc, vp, vp, i32, vp]
+            L.moe_pack_tiled.restype = ctypes.c_int
             pi32, pd = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)
             L.moe_fit_times.argtypes = [ctypes.c_int32, ctypes.c_int32, pi32, pi32, ctypes.c_int32, pd,
                                         ctypes.c_double, pd]

@@ -54,6 +54,7 @@ constexpr int kWaves = 4;  // waves per workgroup (split of K)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16;  // output rows per item = MFMA M
 constexpr int kPerSlot = 0, kDedup = 1;
+constexpr int kLayPlain = 0, kLayPacked = 1, kLayTiled = 2;  // weight layouts (MOE_FLAG_*)
 constexpr uint32_t kOOB = 0x80000000u;       // buffer offset beyond every range: load returns 0
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data
 constexpr int kSpinLimit = 1 << 17;          // bounded wait on a counter (~0.2 s)
@@ -143,22 +144,46 @@ struct Fmt {
 // vector offset per row and the step's k offset is a wave-uniform scalar offset;
 // otherwise each step forms a checked vector offset.  Steps past ns read zeros
 // through an out-of-range vector offset (scalar offset 0).
-template <bool BF16, bool KF>
+// A wave's steps are s0, s0 + SS, s0 + 2 SS, ...: a contiguous range (SS = 1) or,
+// with tiled weights, every kWaves-th step (SS = kWaves).
+template <bool BF16, bool KF, int SS = 1>
 struct Steps {
     using F = Fmt<BF16>;
     int s0, ns, K, q;
     __device__ uint32_t lane_base(uint32_t base) const {
         return KF ? cat(base, (uint32_t)q * 16u) : base;
     }
+    __device__ int step(int i) const { return s0 + SS * i; }
     __device__ uint32_t vofs(uint32_t lb, int i) const {
         if (KF) return i < ns ? lb : kOOB;
-        const int k = (s0 + i) * F::kStep + q * F::kPer;
+        const int k = step(i) * F::kStep + q * F::kPer;
         return (i < ns && k < K) ? cat(lb, (uint32_t)k * F::kEsize) : kOOB;
     }
     __device__ uint32_t sofs(int i) const {
-        return (KF && i < ns) ? (uint32_t)(s0 + i) * (uint32_t)(F::kStep * F::kEsize) : 0u;
+        return (KF && i < ns) ? (uint32_t)step(i) * (uint32_t)(F::kStep * F::kEsize) : 0u;
     }
 };
+
+// Tiled weights: a matrix of R rows and K contraction columns (R a multiple of 16,
+// K of the step) in blocks of 16 rows x one step (64 bytes a row, 1 KB a block);
+// block (r16, s) at byte (r16 * S + s) * 1 KB with S = K / step, and in a block lane
+// l's 16 bytes, row l % 16 and k-group l / 16, at byte 16 l.  One load instruction
+// reads one whole block.  With the wave-interleaved step order (wave w takes steps
+// w, w + 4, ...) the four waves of a work group read adjacent blocks at each step.
+constexpr uint32_t kBlock = 1024;
+struct TSteps {
+    int s0, ns;  // steps s0, s0 + kWaves, ...
+    __device__ static uint32_t lane_base(bool ok, int r16, int S, int lane) {
+        return ok ? (uint32_t)r16 * (uint32_t)S * kBlock + (uint32_t)lane * 16u : kOOB;
+    }
+    __device__ uint32_t vofs(uint32_t lb, int i) const { return i < ns ? lb : kOOB; }
+    __device__ uint32_t sofs(int i) const { return i < ns ? (uint32_t)(s0 + kWaves * i) * kBlock : 0u; }
+};
+
+// steps of [k0, k0 + len) that wave w takes in the interleaved order
+__device__ __forceinline__ int interleaved_steps(int len, int w) {
+    return len > w ? (len - w + kWaves - 1) / kWaves : 0;
+}
 
 // W_down packed in blocks of 8 columns, [N][d_ff/8][d_model][8] (element (i, f) at
 // byte ((f/8)*d + i)*8*E + (f%8)*E): the 8*k-th .. 8*k+7-th hidden columns of all
@@ -332,7 +357,7 @@ __device__ bool wait_count(const int32_t* p, int target) {
 // contributor order and then its own, and finalises h.  Returns true in the work
 // group that finalised the tile.
 // ---------------------------------------------------------------------------
-template <bool BF16, int NT, int RB, bool KF, int P, bool SH>
+template <bool BF16, int NT, int RB, bool KF, int P, bool SH, bool TL>
 __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e, bool sh, int g, int t, int k0,
                                         int k1, int tile, int nc, int j) {
     using F = Fmt<BF16>;
@@ -353,8 +378,11 @@ __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e,
     const auto rx = rsrc(a.x, (uint32_t)(a.n * a.d * F::kEsize));
     int32_t* tc = a.sync + kLine * (MOE_MAX_SLOTS + kMaxDownTiles + tile);  // split tile: partials stored
     const int len = k1 - k0;
-    const int s0 = k0 + wave * len / kWaves;
-    const Steps<BF16, KF> st{s0, k0 + (wave + 1) * len / kWaves - s0, a.d, q};
+    // tiled weights: wave w takes steps k0 + w, k0 + w + 4, ...; else a contiguous quarter
+    const int s0 = TL ? k0 + wave : k0 + wave * len / kWaves;
+    const Steps<BF16, KF, TL ? kWaves : 1> st{s0, TL ? interleaved_steps(len, wave) : k0 + (wave + 1) * len / kWaves - s0,
+                                             a.d, q};
+    const TSteps tst{s0, st.ns};
     const int ns = st.ns;
     // h = silu(G) * U for rows f0 .. f0+3 of slot `slot` (bf16: hi and lo halves)
     auto store_h = [&](f32x4 G, f32x4 Uu, int slot, int f0) {
@@ -384,7 +412,9 @@ __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e,
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const int row = t * RT + rb * kTile + lr;
-        lrow[rb] = st.lane_base(row < a.d_ff ? (uint32_t)row * a.d * F::kEsize : kOOB);
+        const int r16 = t * RB + rb;  // tiled: row block (d_ff a multiple of 16)
+        lrow[rb] = TL ? TSteps::lane_base(r16 * kTile < a.d_ff, r16, a.S1, lane)
+                      : st.lane_base(row < a.d_ff ? (uint32_t)row * a.d * F::kEsize : kOOB);
     }
     for (int base = 0; base < g; base += 16 * NT) {
         uint32_t lx[NT];
@@ -397,10 +427,12 @@ __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e,
         u32x4 ag[P][RB], au[P][RB], bx[P][NT];
         auto issue = [&](int slot, int j) {  // loads of wave step j into ring slot `slot`
             const uint32_t so = st.sofs(j);
+            const uint32_t wo = TL ? tst.sofs(j) : so;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
-                ag[slot][rb] = bload2<0>(rg, st.vofs(lrow[rb], j), so);
-                au[slot][rb] = bload2<0>(ru, st.vofs(lrow[rb], j), so);
+                const uint32_t vo = TL ? tst.vofs(lrow[rb], j) : st.vofs(lrow[rb], j);
+                ag[slot][rb] = bload2<0>(rg, vo, wo);
+                au[slot][rb] = bload2<0>(ru, vo, wo);
             }
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) bx[slot][tt] = bload2<0>(rx, st.vofs(lx[tt], j), so);
@@ -524,9 +556,10 @@ constexpr int kSL = 4;  // register mode: h staging loads in flight per thread
 
 // The per-slot kernel holds its registers to 4 waves per SIMD, so that a small
 // pass's gate/up and down work groups are all resident at once.
-template <bool BF16, int MODE, int NT, int RB, bool KF, bool DPF, bool PK, bool SH>
+template <bool BF16, int MODE, int NT, int RB, bool KF, bool DPF, int LAY, bool SH>
 __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(Args a) {
     using F = Fmt<BF16>;
+    constexpr bool PK = LAY == kLayPacked, TL = LAY == kLayTiled;
     // ring depth in steps: operand registers per step are (2*RB + NT) for gate/up
     // and (RB + 2*NT) for down, 4 VGPRs each
     constexpr int P = (2 * RB + NT) <= 3 ? 8 : ((2 * RB + NT) <= 6 ? 4 : 2);
@@ -611,8 +644,8 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
             // work groups whose shares meet this tile: first .. last
             const int first = uni(split ? ((tile * a.S1 + 1) * a.g1 - 1) / ltot : wi);
             const int last = uni(split ? ((tile * a.S1 + a.S1) * a.g1 - 1) / ltot : wi);
-            const bool fin = gate_up<BF16, NT, RB, KF, P, SH>(a, sm, e, sh, g, t, k0, k1, tile, last - first + 1,
-                                                          wi - first);
+            const bool fin = gate_up<BF16, NT, RB, KF, P, SH, TL>(a, sm, e, sh, g, t, k0, k1, tile,
+                                                              last - first + 1, wi - first);
             if (tid == 0 && fin) atomicAdd(a.sync + kLine * u, 1);  // h-ready count of unit u
         }
         if (want_status && cur < 0) resolve(0, true, e, g, sh);  // an empty share still reports the status
@@ -636,24 +669,30 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
             const auto rl = rsrc(a.h + (BF16 ? hbytes : 0), hbytes);
             const auto ro = rsrc(a.O, (uint32_t)nslot * a.ks * a.d * 4);
             // steps kb .. ke-1 of the d_ff contraction (all of it when ks == 1), split
-            // over the four waves
+            // over the four waves: contiguous quarters, or with tiled weights every
+            // fourth step from kb + wave
             const int S = (a.d_ff + F::kStep - 1) / F::kStep;
             const int kb = kp * S / a.ks, kl = (kp + 1) * S / a.ks - kb;
-            const int s0 = kb + wave * kl / kWaves;
-            const Steps<BF16, KF> st{s0, kb + (wave + 1) * kl / kWaves - s0, a.d_ff, q};
+            const int s0 = TL ? kb + wave : kb + wave * kl / kWaves;
+            const Steps<BF16, KF, TL ? kWaves : 1> st{
+                s0, TL ? interleaved_steps(kl, wave) : kb + (wave + 1) * kl / kWaves - s0, a.d_ff, q};
             const PSteps<BF16, KF> pst{s0, st.ns, a.d_ff, a.d, q};  // W_down packed (PK)
+            const TSteps tst{s0, st.ns};                           // W_down tiled (TL)
             const int ns = st.ns;
             uint32_t lrow[RB2];
 #pragma unroll
             for (int rb = 0; rb < RB2; ++rb) {
                 const int row = t * RT2 + rb * kTile + lr;
-                lrow[rb] = PK ? pst.lane_base(row < a.d, row)
-                              : st.lane_base(row < a.d ? (uint32_t)row * a.d_ff * F::kEsize : kOOB);
+                const int r16 = t * RB2 + rb;  // tiled: row block (d a multiple of 16)
+                lrow[rb] = TL   ? TSteps::lane_base(r16 * kTile < a.d, r16, S, lane)
+                           : PK ? pst.lane_base(row < a.d, row)
+                                : st.lane_base(row < a.d ? (uint32_t)row * a.d_ff * F::kEsize : kOOB);
             }
             // W_down chunk of row block rb at wave step j
             auto wload = [&](int rb, int j) {
-                return PK ? bload2<0>(rd, pst.vofs(lrow[rb], j), pst.sofs(j))
-                          : bload2<0>(rd, st.vofs(lrow[rb], j), st.sofs(j));
+                return TL   ? bload2<0>(rd, tst.vofs(lrow[rb], j), tst.sofs(j))
+                       : PK ? bload2<0>(rd, pst.vofs(lrow[rb], j), pst.sofs(j))
+                            : bload2<0>(rd, st.vofs(lrow[rb], j), st.sofs(j));
             };
             if constexpr (DPF) {
                 // All of this wave's W_down rows go to registers before the wait, so
@@ -706,7 +745,7 @@ __global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(A
 #pragma unroll
                     for (int i = 0; i < kPF; ++i) {
                         if (i < ns) {
-                            const int k = (s0 + i) * F::kStep + q * F::kPer;
+                            const int k = st.step(i) * F::kStep + q * F::kPer;
                             const bool ok = col_ok && k < a.d_ff;
                             const u32x4 bhv = ok ? *reinterpret_cast<const u32x4*>(bp + k * F::kEsize) : zero4();
                             u32x4 blv = zero4();
@@ -1101,6 +1140,27 @@ __global__ __launch_bounds__(256) void k_pack_wdown(const char* __restrict__ src
     }
 }
 
+// Tiled copy of E matrices [R][K] (element size es; R a multiple of 16, K of the
+// 64-byte step): destination piece p (16 bytes) is lane l = p % 64 of block p / 64 =
+// (e, r16, s) in that order, row r16*16 + l%16, columns s*step + (l/16)*(16/es) on.
+// Writes are contiguous; each thread reads one 16-byte piece of a source row.
+__global__ __launch_bounds__(256) void k_pack_tiled(const char* __restrict__ src, char* __restrict__ dst, int64_t E,
+                                                   int R, int K, int es) {
+    const int per = 16 / es, step = 64 / es;
+    const int S = K / step, R16 = R / 16;
+    const int64_t pieces = E * R16 * S * 64;
+    for (int64_t p = blockIdx.x * 256ll + threadIdx.x; p < pieces; p += (int64_t)gridDim.x * 256) {
+        const int l = (int)(p & 63);
+        const int64_t blk = p >> 6;
+        const int s = (int)(blk % S);
+        const int64_t rest = blk / S;
+        const int r16 = (int)(rest % R16);
+        const int64_t e = rest / R16;
+        const int64_t so = ((e * R + r16 * 16 + (l & 15)) * K + (int64_t)s * step + (l >> 4) * per) * es;
+        *reinterpret_cast<u32x4*>(dst + p * 16) = *reinterpret_cast<const u32x4*>(src + so);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Grouping: histogram, exclusive scan and stable scatter of slot indices by
 // expert id, in one workgroup of 256 threads (n*m <= 256, N <= 1024).
@@ -1205,8 +1265,13 @@ int check_desc(const moe_layer_desc* d, int32_t n) {
     if (d->d_model < 8 || d->d_ff < 8 || (d->d_model % 8) || (d->d_ff % 8)) return MOE_E_DTYPE;
     if (d->N < 1 || d->N > MOE_MAX_EXPERTS || d->m < 1 || d->m > d->N) return MOE_E_INVAL;
     if (n < 1 || n > MOE_MAX_TOKENS || (int64_t)n * d->m > MOE_MAX_SLOTS) return MOE_E_INVAL;
-    if (d->flags & ~(MOE_FLAG_ACCUMULATE | MOE_FLAG_WDOWN_PACKED)) return MOE_E_INVAL;
+    if (d->flags & ~(MOE_FLAG_ACCUMULATE | MOE_FLAG_WDOWN_PACKED | MOE_FLAG_TILED)) return MOE_E_INVAL;
     const int64_t es = d->dtype == MOE_BF16 ? 2 : 4;
+    // tiled weights: one layout of all three matrices, both contractions whole steps
+    if (d->flags & MOE_FLAG_TILED) {
+        if (d->flags & MOE_FLAG_WDOWN_PACKED) return MOE_E_INVAL;
+        if (d->d_model % (64 / es) || d->d_ff % (64 / es)) return MOE_E_INVAL;
+    }
     // one expert matrix must be addressable by a 31-bit buffer offset
     if ((int64_t)d->d_model * d->d_ff * es > (1ll << 31) - 4096) return MOE_E_INVAL;
     if ((d->d_model + kTile - 1) / kTile > kMaxDownTiles) return MOE_E_INVAL;  // d_model <= 16384
@@ -1298,43 +1363,45 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     return p;
 }
 
-template <bool BF16, int MODE, int NT, int RB, bool PK, bool SH>
-void launch_pk(const Args& args, const Plan& p, int grid, hipStream_t st) {
+template <bool BF16, int MODE, int NT, int RB, int LAY, bool SH>
+void launch_lay(const Args& args, const Plan& p, int grid, hipStream_t st) {
     constexpr int step = Fmt<BF16>::kStep;
-    const bool kf = args.d % step == 0 && args.d_ff % step == 0;
+    // tiled weights have K a multiple of the step in both contractions (check_desc)
+    const bool kf = LAY == kLayTiled || (args.d % step == 0 && args.d_ff % step == 0);
     if (kf && p.dpf)
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, true, PK, SH>), dim3(grid), dim3(kThreads), p.lds, st,
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, true, LAY, SH>), dim3(grid), dim3(kThreads), p.lds, st,
                            args);
     else if (kf)
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, false, PK, SH>), dim3(grid), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, false, LAY, SH>), dim3(grid), dim3(kThreads), 0, st,
                            args);
-    else if (p.dpf)
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, true, PK, SH>), dim3(grid), dim3(kThreads), p.lds, st,
-                           args);
-    else
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, false, PK, SH>), dim3(grid), dim3(kThreads), 0, st,
-                           args);
+    else if constexpr (LAY != kLayTiled) {
+        if (p.dpf)
+            hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, true, LAY, SH>), dim3(grid), dim3(kThreads), p.lds,
+                               st, args);
+        else
+            hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, false, LAY, SH>), dim3(grid), dim3(kThreads), 0, st,
+                               args);
+    }
+}
+
+template <bool BF16, int MODE, int NT, int RB, bool SH>
+void launch_rb(const Args& args, const Plan& p, int grid, hipStream_t st, int lay) {
+    if (lay == kLayTiled) launch_lay<BF16, MODE, NT, RB, kLayTiled, SH>(args, p, grid, st);
+    else if (lay == kLayPacked) launch_lay<BF16, MODE, NT, RB, kLayPacked, SH>(args, p, grid, st);
+    else launch_lay<BF16, MODE, NT, RB, kLayPlain, SH>(args, p, grid, st);
 }
 
 // Kernel variant for the plan.  Shared experts (SH) are a variant of their own, so
 // that passes without them carry none of their registers; a per-slot pass without
 // them always takes one token column tile.
 template <bool BF16, int MODE, bool SH>
-void launch_nt(const Args& args, const Plan& p, int grid, hipStream_t st, bool pk) {
+void launch_nt(const Args& args, const Plan& p, int grid, hipStream_t st, int lay) {
     if constexpr (MODE == kPerSlot && !SH) {
-        if (pk) launch_pk<BF16, MODE, 1, 2, true, SH>(args, p, grid, st);
-        else launch_pk<BF16, MODE, 1, 2, false, SH>(args, p, grid, st);
+        launch_rb<BF16, MODE, 1, 2, SH>(args, p, grid, st, lay);
     } else {
-        if (p.nt == 1) {
-            if (pk) launch_pk<BF16, MODE, 1, 2, true, SH>(args, p, grid, st);
-            else launch_pk<BF16, MODE, 1, 2, false, SH>(args, p, grid, st);
-        } else if (p.nt == 2) {
-            if (pk) launch_pk<BF16, MODE, 2, 2, true, SH>(args, p, grid, st);
-            else launch_pk<BF16, MODE, 2, 2, false, SH>(args, p, grid, st);
-        } else {
-            if (pk) launch_pk<BF16, MODE, 4, 1, true, SH>(args, p, grid, st);
-            else launch_pk<BF16, MODE, 4, 1, false, SH>(args, p, grid, st);
-        }
+        if (p.nt == 1) launch_rb<BF16, MODE, 1, 2, SH>(args, p, grid, st, lay);
+        else if (p.nt == 2) launch_rb<BF16, MODE, 2, 2, SH>(args, p, grid, st, lay);
+        else launch_rb<BF16, MODE, 4, 1, SH>(args, p, grid, st, lay);
     }
 }
 
@@ -1397,14 +1464,14 @@ int run_expert(const moe_layer_desc* d, const moe_layer_weights* W, const void* 
     (void)hipGetLastError();
     if (events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(events[0]), st);
     const bool bf = d->dtype == MOE_BF16;
-    const bool pk = (d->flags & MOE_FLAG_WDOWN_PACKED) != 0;
+    const int lay = (d->flags & MOE_FLAG_TILED) ? kLayTiled : (d->flags & MOE_FLAG_WDOWN_PACKED) ? kLayPacked : kLayPlain;
     const bool sh = d->n_shared > 0;
     if (bf) {
-        if (sh) launch_nt<true, MODE, true>(args, p, grid, st, pk);
-        else launch_nt<true, MODE, false>(args, p, grid, st, pk);
+        if (sh) launch_nt<true, MODE, true>(args, p, grid, st, lay);
+        else launch_nt<true, MODE, false>(args, p, grid, st, lay);
     } else {
-        if (sh) launch_nt<false, MODE, true>(args, p, grid, st, pk);
-        else launch_nt<false, MODE, false>(args, p, grid, st, pk);
+        if (sh) launch_nt<false, MODE, true>(args, p, grid, st, lay);
+        else launch_nt<false, MODE, false>(args, p, grid, st, lay);
     }
     if (events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(events[1]), st);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
@@ -1474,6 +1541,29 @@ int moe_pack_w_down(const moe_layer_desc* desc, const void* w_down, void* w_down
     hipLaunchKernelGGL(k_pack_wdown, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(hip_stream),
                        reinterpret_cast<const char*>(w_down), reinterpret_cast<char*>(w_down_packed),
                        (int64_t)desc->N, desc->d_model, desc->d_ff, (int)es);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+int moe_pack_tiled(const moe_layer_desc* desc, const void* w, void* w_tiled, int32_t mat, void* hip_stream) {
+    if (!desc || (mat != MOE_MAT_GATE_UP && mat != MOE_MAT_DOWN)) return MOE_E_INVAL;
+    moe_layer_desc dd = *desc;
+    dd.flags = MOE_FLAG_TILED;
+    dd.n_shared = 0;
+    const int rc = check_desc(&dd, 1);
+    if (rc != MOE_OK) return rc;
+    if (!w || !w_tiled || !aligned16(w) || !aligned16(w_tiled)) return MOE_E_INVAL;
+    const int64_t es = desc->dtype == MOE_BF16 ? 2 : 4;
+    const int64_t bytes = (int64_t)desc->N * desc->d_model * desc->d_ff * es;
+    const char* a0 = reinterpret_cast<const char*>(w);
+    const char* b0 = reinterpret_cast<const char*>(w_tiled);
+    if (a0 < b0 + bytes && b0 < a0 + bytes) return MOE_E_INVAL;  // overlapping
+    const int R = mat == MOE_MAT_GATE_UP ? desc->d_ff : desc->d_model;
+    const int K = mat == MOE_MAT_GATE_UP ? desc->d_model : desc->d_ff;
+    const int64_t pieces = bytes / 16;
+    const int grid = (int)std::min<int64_t>((pieces + 255) / 256, 65536);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_pack_tiled, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(hip_stream), a0,
+                       reinterpret_cast<char*>(w_tiled), (int64_t)desc->N, R, K, (int)es);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 

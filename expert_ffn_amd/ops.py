@@ -46,15 +46,19 @@ def _check_dev(name, t, dtype=None, shape=None):
 class Layer:
     """Device weights of one MoE layer: W_gate, W_up [N][d_ff][d], W_down [N][d][d_ff],
     or, with ``packed``, W_down in the layout of ``moe_pack_w_down``,
-    [N][d_ff/8][d][8] (see ``Layer.packed_copy``).  ``shared``: the always-on
-    experts' (W_gate, W_up, W_down), [n_shared][...] in the same layouts, computed in
-    the same call as the routed experts."""
+    [N][d_ff/8][d][8] (see ``Layer.packed_copy``), or, with ``tiled``, all three in
+    the tiled layout of ``moe_pack_tiled`` (same shapes, see ``Layer.tiled_copy``).
+    ``shared``: the always-on experts' (W_gate, W_up, W_down), [n_shared][...] in the
+    same layouts, computed in the same call as the routed experts."""
 
-    def __init__(self, w_gate, w_up, w_down, m, packed=False, shared=None):
+    def __init__(self, w_gate, w_up, w_down, m, packed=False, shared=None, tiled=False):
         N, d_ff, d = w_gate.shape
         _check_dev("w_gate", w_gate)
         _check_dev("w_up", w_up, w_gate.dtype, (N, d_ff, d))
+        if packed and tiled:
+            raise ValueError("a layer is either packed (W_down) or tiled (all three)")
         self.packed = bool(packed)
+        self.tiled = bool(tiled)
         self.N, self.m, self.d, self.d_ff = N, int(m), d, d_ff
         self.dtype = w_gate.dtype
         _check_dev("w_down", w_down, w_gate.dtype, self._down_shape(N))
@@ -79,7 +83,8 @@ class Layer:
         return (E, self.d_ff // 8, self.d, 8) if self.packed else (E, self.d, self.d_ff)
 
     def desc(self, accumulate=False):
-        flags = (_abi.MOE_FLAG_ACCUMULATE if accumulate else 0) | (_abi.MOE_FLAG_WDOWN_PACKED if self.packed else 0)
+        flags = ((_abi.MOE_FLAG_ACCUMULATE if accumulate else 0) | (_abi.MOE_FLAG_WDOWN_PACKED if self.packed else 0)
+                 | (_abi.MOE_FLAG_TILED if self.tiled else 0))
         return _abi.LayerDesc(self.N, self.m, self.d, self.d_ff, _dtype_code(self.w_gate), flags, self.n_shared)
 
     def packed_copy(self, stream=None):
@@ -87,6 +92,8 @@ class Layer:
         ``moe_pack_w_down`` (new device tensors; W_gate and W_up shared)."""
         if self.packed:
             return self
+        if self.tiled:
+            raise ValueError("a tiled layer cannot also be packed")
 
         def pk(wd):
             E = wd.shape[0]
@@ -95,9 +102,27 @@ class Layer:
         sh = None if self.shared is None else (self.shared[0], self.shared[1], pk(self.shared[2]))
         return Layer(self.w_gate, self.w_up, pk(self.w_down), self.m, packed=True, shared=sh)
 
+    def tiled_copy(self, stream=None):
+        """The same layer with W_gate, W_up and W_down (routed and shared) copied into
+        the tiled layout by ``moe_pack_tiled`` (new device tensors of the same
+        shapes)."""
+        if self.tiled:
+            return self
+        if self.packed:
+            raise ValueError("tile a layer from its plain layout")
+
+        def tl(w, mat):
+            return pack_tiled(self, w, torch.empty_like(w), mat, stream=stream)
+        G, D = _abi.MOE_MAT_GATE_UP, _abi.MOE_MAT_DOWN
+        sh = None
+        if self.shared is not None:
+            sg, su, sd = self.shared
+            sh = (tl(sg, G), tl(su, G), tl(sd, D))
+        return Layer(tl(self.w_gate, G), tl(self.w_up, G), tl(self.w_down, D), self.m, shared=sh, tiled=True)
+
     def without_shared(self):
         """The routed experts alone (same tensors)."""
-        return Layer(self.w_gate, self.w_up, self.w_down, self.m, packed=self.packed)
+        return Layer(self.w_gate, self.w_up, self.w_down, self.m, packed=self.packed, tiled=self.tiled)
 
     @property
     def expert_bytes(self):
@@ -119,6 +144,20 @@ def pack_w_down(layer, w_down, out, stream=None):
     _check_dev("out", out, layer.dtype, (E, layer.d_ff // 8, layer.d, 8))
     desc = _abi.LayerDesc(E, 1, layer.d, layer.d_ff, _dtype_code(layer.w_gate), 0, 0)
     check("moe_pack_w_down", lib().moe_pack_w_down(ctypes.byref(desc), _vp(w_down), _vp(out), _stream(stream)))
+    return out
+
+
+def pack_tiled(layer, w, out, mat, stream=None):
+    """Copy one weight tensor of E experts (the layer's N, or its shared experts) into
+    the tiled layout of ``moe_pack_tiled`` (one launch): ``mat`` MOE_MAT_GATE_UP for
+    W_gate or W_up [E][d_ff][d], MOE_MAT_DOWN for W_down [E][d][d_ff]; ``out`` has the
+    source's shape."""
+    E = w.shape[0]
+    shape = (E, layer.d_ff, layer.d) if mat == _abi.MOE_MAT_GATE_UP else (E, layer.d, layer.d_ff)
+    _check_dev("w", w, layer.dtype, shape)
+    _check_dev("out", out, layer.dtype, shape)
+    desc = _abi.LayerDesc(E, 1, layer.d, layer.d_ff, _dtype_code(layer.w_gate), 0, 0)
+    check("moe_pack_tiled", lib().moe_pack_tiled(ctypes.byref(desc), _vp(w), _vp(out), int(mat), _stream(stream)))
     return out
 
 

@@ -28,7 +28,8 @@
  *     all accumulation is fp32; y is fp32.
  *   - Weight layouts, row-major and contiguous:
  *         W_gate, W_up : [N][d_ff][d_model]      W_down : [N][d_model][d_ff]
- *     (or W_down packed by moe_pack_w_down, flagged MOE_FLAG_WDOWN_PACKED);
+ *     (or W_down packed by moe_pack_w_down, flagged MOE_FLAG_WDOWN_PACKED, or all
+ *     three tiled by moe_pack_tiled, flagged MOE_FLAG_TILED);
  *     x : [n][d_model];  ids : [n][m] int32;  w : [n][m] fp32;  y : [n][d_model].
  *   - Workspaces (`ws`) are caller-owned device memory that must be zero-filled
  *     once before first use (e.g. hipMemset); every call that runs to completion
@@ -65,6 +66,12 @@ enum { MOE_KIND_SLOT = 0, MOE_KIND_DEDUP = 1 };
 #define MOE_FLAG_ACCUMULATE 1u /* y += result (else y = result) */
 /* w_down is in the packed layout of moe_pack_w_down (else [N][d_model][d_ff]) */
 #define MOE_FLAG_WDOWN_PACKED 2u
+/* w_gate, w_up and w_down (routed and shared) are all in the tiled layout of
+ * moe_pack_tiled; excludes MOE_FLAG_WDOWN_PACKED */
+#define MOE_FLAG_TILED 4u
+/* matrices of moe_pack_tiled */
+#define MOE_MAT_GATE_UP 0 /* W_gate or W_up [N][d_ff][d_model]: rows d_ff, contraction d_model */
+#define MOE_MAT_DOWN 1    /* W_down [N][d_model][d_ff]: rows d_model, contraction d_ff */
 
 /* One MoE layer.  1 <= m <= N (m == N is allowed, so that always-on experts can
  * also run as a layer of their own whose every token selects all of them). */
@@ -200,6 +207,32 @@ int moe_expert_auto(const moe_layer_desc* desc, const moe_layer_weights* weights
  * arguments (nothing enqueued), or MOE_E_HIP. */
 int moe_pack_w_down(const moe_layer_desc* desc, const void* w_down, void* w_down_packed,
                     void* hip_stream);
+
+/*
+ * moe_pack_tiled -- copy one weight tensor of desc->N experts into the tiled
+ * layout that expert calls read when desc->flags has MOE_FLAG_TILED (then W_gate,
+ * W_up and W_down, routed and shared, must all be tiled).  The tensor is
+ * [N][R][K]: rows R and contraction K are (d_ff, d_model) for MOE_MAT_GATE_UP and
+ * (d_model, d_ff) for MOE_MAT_DOWN.  With step = 64 bytes / element size (32 bf16 or
+ * 16 fp32 elements), both d_model and d_ff must be multiples of the step.  The
+ * copy is made of 1024-byte blocks, 16 rows x one step each, in (expert, row
+ * block, step) order; in block (e, r, s), lane l = 0..63 holds 16 bytes at 16*l:
+ * row 16*r + l%16, the 16/size elements from column step*s + (l/16)*(16/size).  Same
+ * byte size as the source.  The row-block-and-step blocks are the operands of one
+ * 16-row MFMA step (weights of the matrix operand in the lane order the
+ * instruction takes), so one load instruction of a wave reads one whole block,
+ * and the four waves of a work group, which take every fourth step, read
+ * adjacent blocks.  Same result as the plain layout up to the fp32 summation
+ * order.  A weight-load-time step, not part of the expert operation (Lan,
+ * Section 1: the per-expert feed-forward W_down (silu(W_gate x) * W_up x); the
+ * layout is this library's).  Shared experts are packed with desc->N = n_shared.
+ *   w, w_tiled  device, 16-byte aligned, not overlapping; desc->flags and
+ *               desc->n_shared are ignored.
+ * Asynchronous on hip_stream.  Returns MOE_OK, MOE_E_INVAL for a bad matrix code,
+ * pointers or sizes that are not whole steps, MOE_E_DTYPE for a bad dtype (nothing
+ * enqueued), or MOE_E_HIP. */
+int moe_pack_tiled(const moe_layer_desc* desc, const void* w, void* w_tiled, int32_t mat,
+                   void* hip_stream);
 
 /*
  * moe_router_topk -- the router ahead of the expert operation: it sends each token

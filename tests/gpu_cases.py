@@ -16,6 +16,16 @@ SYNC_BYTES = 4 * 32 * (256 + 1024 + 512)  # counter area at the start of a works
 SUMMATION_TOL = 1e-4  # rel-L2 between per-slot and dedup results (fp32 summation order)
 
 
+# weight layouts: as given, W_down packed, all three tiled
+LAYOUTS = ("plain", "packed", "tiled")
+
+
+def step_multiple(v, dtype):
+    """v rounded up to a whole 64-byte step of the dtype (the tiled layout's unit)."""
+    step = 32 if dtype == "bf16" else 16
+    return -(-v // step) * step
+
+
 def say(*a):
     print("[case]", *a, flush=True)
     sys.stdout.flush()
@@ -27,7 +37,10 @@ class DeviceLayer:
     n_shared, run as a second call) and ``fused`` the routed and shared experts as
     one layer (one call)."""
 
-    def __init__(self, spec, seed, layer=0, with_shared=False, host=None, packed=False):
+    def __init__(self, spec, seed, layer=0, with_shared=False, host=None, packed=False, layout=None):
+        layout = layout or ("packed" if packed else "plain")
+        assert layout in LAYOUTS, layout
+        self.layout = layout
         self.spec = spec
         self.host = host if host is not None else synth.layer_weights(spec, seed, layer)
         self.dev = efa.Layer(*(to_torch(a) for a in self.host), m=spec.m)
@@ -40,11 +53,12 @@ class DeviceLayer:
             sd = self.shared_dev
             self.fused = efa.Layer(self.dev.w_gate, self.dev.w_up, self.dev.w_down, m=spec.m,
                                    shared=(sd.w_gate, sd.w_up, sd.w_down))
-        if packed:  # W_down in the packed layout (moe_pack_w_down); the plain copies are dropped
-            self.dev = self.dev.packed_copy()
+        if layout != "plain":  # W_down packed (moe_pack_w_down) or all three tiled (moe_pack_tiled)
+            cp = (lambda L: L.packed_copy()) if layout == "packed" else (lambda L: L.tiled_copy())
+            self.dev = cp(self.dev)
             if self.fused is not None:
-                self.fused = self.fused.packed_copy()
-                self.shared_dev = self.shared_dev.packed_copy()
+                self.fused = cp(self.fused)
+                self.shared_dev = cp(self.shared_dev)
             torch.cuda.synchronize()
 
     def run(self, x_host, ids_host, w_host, shared=False, stream=None):

@@ -52,7 +52,12 @@ def test_host_validation_rejects_before_launch():
         (_desc(d_model=60), _abi.MOE_E_DTYPE),
         (_desc(d_ff=100), _abi.MOE_E_DTYPE),
         (_desc(dtype=7), _abi.MOE_E_DTYPE),
-        (_desc(flags=4), _abi.MOE_E_INVAL),
+        (_desc(flags=8), _abi.MOE_E_INVAL),  # unknown flag bit
+        # tiled weights: not together with packed W_down, and only for whole 64-byte steps
+        (_desc(flags=_abi.MOE_FLAG_TILED | _abi.MOE_FLAG_WDOWN_PACKED), _abi.MOE_E_INVAL),
+        (_desc(flags=_abi.MOE_FLAG_TILED, d_model=40), _abi.MOE_E_INVAL),
+        (_desc(flags=_abi.MOE_FLAG_TILED, d_ff=136), _abi.MOE_E_INVAL),
+        (_desc(flags=_abi.MOE_FLAG_TILED, dtype=_abi.MOE_BF16, d_model=48), _abi.MOE_E_INVAL),
         (_desc(N=2000, m=2), _abi.MOE_E_INVAL),
     ]
     for desc, want in cases:
@@ -126,6 +131,31 @@ def test_host_validation_rejects_before_launch():
     assert L.moe_route_group(fake, 129, 2, 8, fake, fake, fake, fake, fake, None) == _abi.MOE_E_INVAL
     assert L.moe_route_group(fake, 4, 9, 8, fake, fake, fake, fake, fake, None) == _abi.MOE_E_INVAL
     assert L.moe_route_group(None, 4, 2, 8, fake, fake, fake, fake, fake, None) == _abi.MOE_E_INVAL
+
+
+def test_pack_tiled_host_validation():
+    """moe_pack_tiled rejects a bad matrix code, sizes that are not whole steps, null,
+    misaligned or overlapping pointers, before any launch; the tiled flag is accepted
+    (a workspace size) exactly where the layout is defined."""
+    L = _abi.lib()
+    vp = ctypes.c_void_p
+    a, b = vp(0x100000), vp(0x900000)
+    d = _desc()  # fp32, d_model 64, d_ff 128, 8 experts: 256 KiB a tensor
+    for mat in (-1, 2):
+        assert L.moe_pack_tiled(ctypes.byref(d), a, b, mat, None) == _abi.MOE_E_INVAL
+    for mat in (_abi.MOE_MAT_GATE_UP, _abi.MOE_MAT_DOWN):
+        assert L.moe_pack_tiled(ctypes.byref(_desc(d_model=40)), a, b, mat, None) == _abi.MOE_E_INVAL
+        assert L.moe_pack_tiled(ctypes.byref(_desc(dtype=_abi.MOE_BF16, d_ff=144)), a, b, mat, None) == _abi.MOE_E_INVAL
+        assert L.moe_pack_tiled(ctypes.byref(_desc(dtype=9)), a, b, mat, None) == _abi.MOE_E_DTYPE
+        assert L.moe_pack_tiled(ctypes.byref(d), None, b, mat, None) == _abi.MOE_E_INVAL
+        assert L.moe_pack_tiled(ctypes.byref(d), a, None, mat, None) == _abi.MOE_E_INVAL
+        assert L.moe_pack_tiled(ctypes.byref(d), vp(0x100008), b, mat, None) == _abi.MOE_E_INVAL
+        assert L.moe_pack_tiled(ctypes.byref(d), a, vp(0x100000 + 4096), mat, None) == _abi.MOE_E_INVAL  # overlap
+    assert L.moe_pack_tiled(None, a, b, 0, None) == _abi.MOE_E_INVAL
+    T = _abi.MOE_FLAG_TILED
+    assert L.moe_workspace_bytes(ctypes.byref(_desc(flags=T)), 4, 0) == L.moe_workspace_bytes(ctypes.byref(_desc()), 4, 0)
+    assert L.moe_workspace_bytes(ctypes.byref(_desc(flags=T, dtype=_abi.MOE_BF16, d_model=2048, d_ff=1408)), 4, 0) > 0
+    assert L.moe_workspace_bytes(ctypes.byref(_desc(flags=T, dtype=_abi.MOE_BF16, d_ff=144)), 4, 0) == 0
 
 
 @pytest.mark.parametrize("cfg", ["tiny", "dsv2lite", "qwen3", "mixtral"])

@@ -18,7 +18,7 @@ import synth
 from synth import routing
 from synth.device import to_torch
 
-from .gpu_cases import SUMMATION_TOL, DeviceLayer, assert_close, errors, say
+from .gpu_cases import LAYOUTS, SUMMATION_TOL, DeviceLayer, assert_close, errors, say, step_multiple
 
 pytestmark = pytest.mark.gpu
 
@@ -94,12 +94,38 @@ def test_pack_w_down_bit_exact(dtype, shape):
                        ref.view(torch.int16 if dtype == "bf16" else torch.int32))
 
 
-@pytest.mark.parametrize("packed", [False, True])
-def test_tiny_fp32_many_seeds(packed):
+@pytest.mark.parametrize("dtype,E,R,K", [("bf16", 3, 64, 96), ("bf16", 2, 1408, 2048), ("bf16", 2, 2048, 1408),
+                                         ("f32", 4, 48, 80), ("f32", 1, 16, 16)])
+@pytest.mark.parametrize("mat", [efa.MOE_MAT_GATE_UP, efa.MOE_MAT_DOWN])
+def test_pack_tiled_bit_exact(dtype, E, R, K, mat):
+    """moe_pack_tiled against the layout definition: block (e, r, s) of 16 rows x one
+    64-byte step, lane l = 16 q + i holding row 16 r + i, elements s*step + q*per on,
+    i.e. tiled[e][r][s][q][i][:] = W[e][16 r + i][s*step + q*per : +per]."""
+    say("pack tiled", dtype, E, R, K, mat)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    per = 8 if dtype == "bf16" else 4
+    step = 4 * per
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12)
+    w = torch.randn(E, R, K, generator=g, device="cuda").to(tdt)
+    # a layer whose (d_ff, d) make the matrix [R][K]: gate/up rows d_ff, down rows d
+    d_ff, d = (R, K) if mat == efa.MOE_MAT_GATE_UP else (K, R)
+    z = torch.zeros(1, d_ff, d, dtype=tdt, device="cuda")
+    layer = efa.Layer(z, z, torch.zeros(1, d, d_ff, dtype=tdt, device="cuda"), m=1)
+    out = torch.full_like(w, 7)
+    efa.pack_tiled(layer, w, out, mat)
+    torch.cuda.synchronize()
+    ref = w.cpu().reshape(E, R // 16, 16, K // step, 4, per).permute(0, 1, 3, 4, 2, 5).contiguous()
+    iv = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(out.cpu().view(iv).reshape(-1), ref.view(iv).reshape(-1))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_tiny_fp32_many_seeds(layout):
     spec = synth.CONFIGS["tiny"]
-    for seed in range(30 if not packed else 10):
-        say("tiny seed", seed, "packed", packed)
-        dl = DeviceLayer(spec, seed, packed=packed)
+    for seed in range(30 if layout == "plain" else 10):
+        say("tiny seed", seed, "layout", layout)
+        dl = DeviceLayer(spec, seed, layout=layout)
         tr = routing.uniform_trace(spec.N, spec.m, 4, routing.rng_for(seed, 0, "uniform"))
         x = synth.pass_x(spec, seed, 0, 0, 4)
         (rel, mx), _ = _compare(dl, x, tr.ids, tr.w, "tiny seed %d" % seed)
@@ -117,20 +143,22 @@ def test_tiny_fp32_many_seeds(packed):
     (40, 4, 72, 1000, 3), (40, 4, 200, 520, 5),
     # multiples of 32, fewer tiles than half the compute units (each tile cut in two)
     (6, 3, 96, 160, 1), (6, 3, 96, 160, 8), (33, 8, 256, 64, 7), (4, 4, 64, 96, 8), (12, 6, 512, 352, 5)])
-@pytest.mark.parametrize("packed", [False, True])
-def test_ragged_shapes(dtype, N, m, d, d_ff, n, packed):
-    say("ragged", dtype, N, m, d, d_ff, n, "packed", packed)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_ragged_shapes(dtype, N, m, d, d_ff, n, layout):
+    if layout == "tiled":  # the same case with d and d_ff in whole steps (tiles, tails and parts stay ragged)
+        d, d_ff = step_multiple(d, dtype), step_multiple(d_ff, dtype)
+    say("ragged", dtype, N, m, d, d_ff, n, "layout", layout)
     spec = synth.layer_spec("tiny", N=N, m=m, d=d, d_ff=d_ff, dtype=dtype, sigma=0.05)
-    dl = DeviceLayer(spec, 17, packed=packed)
+    dl = DeviceLayer(spec, 17, layout=layout)
     tr = routing.correlated_trace(N, m, n, 0.7, routing.rng_for(17, 0, "correlated"))
     x = synth.pass_x(spec, 17, 0, 1, n)
     _compare(dl, x, tr.ids, tr.w, "ragged")
 
 
-@pytest.mark.parametrize("packed", [False, True])
-def test_max_reuse_and_no_reuse(packed):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_max_reuse_and_no_reuse(layout):
     spec = synth.layer_spec("tiny", N=70, m=4, d=128, d_ff=96, dtype="bf16")
-    dl = DeviceLayer(spec, 3, packed=packed)
+    dl = DeviceLayer(spec, 3, layout=layout)
     rng = np.random.default_rng(3)
     for n in (1, 8, 16, 17, 32, 33, 64):
         say("max reuse n", n)
@@ -145,10 +173,10 @@ def test_max_reuse_and_no_reuse(packed):
     _compare(dl, synth.pass_x(spec, 3, 0, 99, 17), ids, w, "no reuse")
 
 
-@pytest.mark.parametrize("packed", [False, True])
-def test_invalid_ids_skip_slot_and_flag(packed):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_invalid_ids_skip_slot_and_flag(layout):
     spec = synth.layer_spec("tiny", N=8, m=2, d=64, d_ff=64, dtype="bf16")
-    dl = DeviceLayer(spec, 5, packed=packed)
+    dl = DeviceLayer(spec, 5, layout=layout)
     ids = np.array([[0, 3], [5, 9], [2, 1]], np.int32)   # slot (1,1) out of range
     w = np.array([[0.5, 0.5], [0.7, 0.3], [0.6, 0.4]], np.float32)
     x = synth.pass_x(spec, 5, 0, 0, 3)
@@ -165,10 +193,10 @@ def test_invalid_ids_skip_slot_and_flag(packed):
     _agree(ys, yd, "invalid")
 
 
-@pytest.mark.parametrize("packed", [False, True])
-def test_accumulate_and_determinism(packed):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_accumulate_and_determinism(layout):
     spec = synth.layer_spec("tiny", N=16, m=4, d=256, d_ff=128, dtype="bf16")
-    dl = DeviceLayer(spec, 8, packed=packed)
+    dl = DeviceLayer(spec, 8, layout=layout)
     tr = routing.uniform_trace(16, 4, 6, routing.rng_for(8, 0, "uniform"))
     x = synth.pass_x(spec, 8, 0, 0, 6)
     say("determinism")
@@ -203,10 +231,22 @@ def dsv2p(dsv2):
     return dl
 
 
+@pytest.fixture(scope="module")
+def dsv2t(dsv2):
+    """The same layer with all three matrices tiled."""
+    say("tile dsv2lite layer")
+    return DeviceLayer(dsv2.spec, 2026, with_shared=True, host=dsv2.host, layout="tiled")
+
+
+@pytest.fixture(scope="module")
+def dsv2_by_layout(dsv2, dsv2p, dsv2t):
+    return {"plain": dsv2, "packed": dsv2p, "tiled": dsv2t}
+
+
 @pytest.mark.parametrize("kind", ["uniform", "correlated"])
-@pytest.mark.parametrize("packed", [False, True])
-def test_dsv2lite_windows(dsv2, dsv2p, kind, packed):
-    dsv2 = dsv2p if packed else dsv2
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_dsv2lite_windows(dsv2_by_layout, kind, layout):
+    dsv2 = dsv2_by_layout[layout]
     spec = dsv2.spec
     tr = routing.make_trace(spec, kind, 512, seed=2026, p=0.5)
     starts = routing.window_starts(512, 8, 8, seed=2026)
@@ -221,26 +261,29 @@ def test_dsv2lite_windows(dsv2, dsv2p, kind, packed):
 
 @pytest.mark.parametrize("base,n_shared,d,d_ff", [("tiny", 1, 64, 128), ("tiny", 3, 72, 40),
                                                    ("dsv2lite", 2, 96, 160), ("dsv2lite", 1, 256, 352)])
-@pytest.mark.parametrize("packed", [False, True])
-def test_shared_experts_in_the_same_call(base, n_shared, d, d_ff, packed):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_shared_experts_in_the_same_call(base, n_shared, d, d_ff, layout):
     """Always-on experts computed in the same launch as the routed ones (each read once
     per pass against all n tokens, weight 1), for both kernels, against the oracle's
     shared-expert sum; n = 17 and 20 take two token columns per MFMA pass."""
+    if layout == "tiled":
+        d, d_ff = step_multiple(d, "bf16"), step_multiple(d_ff, "bf16")
     spec = synth.layer_spec(base, N=12, m=3, d=d, d_ff=d_ff, n_shared=n_shared)
-    dl = DeviceLayer(spec, 31, with_shared=True, packed=packed)
+    dl = DeviceLayer(spec, 31, with_shared=True, layout=layout)
     tr = routing.make_trace(spec, "correlated", 64, seed=31, p=0.5)
     for n in (1, 2, 5, 8, 17, 20):
         ids, w = routing.window(tr, 3, n)
         x = synth.pass_x(spec, 31, 0, n, n)
-        say("shared", base, n_shared, d, d_ff, "packed", packed, "n", n)
+        say("shared", base, n_shared, d, d_ff, "layout", layout, "n", n)
         _compare(dl, x, ids, w, "shared %s S=%d n=%d" % (base, n_shared, n), shared="fused")
 
 
-def test_shared_experts_accumulate_and_most_units():
+@pytest.mark.parametrize("layout", ["packed", "tiled"])
+def test_shared_experts_accumulate_and_most_units(layout):
     """With MOE_FLAG_ACCUMULATE the fused call adds to y; a pass at the unit limit
     (n*m + n_shared = 256) still matches the oracle."""
     spec = synth.layer_spec("dsv2lite", N=64, m=4, d=128, d_ff=96, n_shared=4)
-    dl = DeviceLayer(spec, 5, with_shared=True, packed=True)
+    dl = DeviceLayer(spec, 5, with_shared=True, layout=layout)
     tr = routing.make_trace(spec, "uniform", 128, seed=5)
     n = 63  # 63*4 + 4 = 256 units
     ids, w = routing.window(tr, 0, n)
@@ -260,11 +303,11 @@ def test_shared_experts_accumulate_and_most_units():
         assert_close(y.cpu().numpy() - y0.cpu().numpy(), ref, "accumulate " + fn.__name__)
 
 
-@pytest.mark.parametrize("packed", [False, True])
-def test_qwen3_layer_zipf_and_tree(packed):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_qwen3_layer_zipf_and_tree(layout):
     spec = synth.CONFIGS["qwen3"]
-    say("upload qwen3 layer", "packed", packed)
-    dl = DeviceLayer(spec, 77, layer=3, packed=packed)
+    say("upload qwen3 layer", "layout", layout)
+    dl = DeviceLayer(spec, 77, layer=3, layout=layout)
     tr = routing.make_trace(spec, "zipf", 256, seed=77, layer=3, s=1.1)
     for n in (1, 2, 4, 8):
         ids, w = routing.window(tr, 5 * n, n)
@@ -277,11 +320,11 @@ def test_qwen3_layer_zipf_and_tree(packed):
     _compare(dl, x, ttr.ids, ttr.w, "tree", tokens=[0, 1, 7, 19, 31])
 
 
-@pytest.mark.parametrize("packed", [False, True])
-def test_mixtral_sampled_tokens(packed):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_mixtral_sampled_tokens(layout):
     spec = synth.CONFIGS["mixtral"]
-    say("upload mixtral layer", "packed", packed)
-    dl = DeviceLayer(spec, 9, packed=packed)
+    say("upload mixtral layer", "layout", layout)
+    dl = DeviceLayer(spec, 9, layout=layout)
     tr = routing.make_trace(spec, "correlated", 64, seed=9, p=0.6)
     for n, toks in ((1, [0]), (3, [0, 2]), (8, [1, 6])):
         ids, w = routing.window(tr, 10, n)
@@ -291,13 +334,13 @@ def test_mixtral_sampled_tokens(packed):
 
 
 @pytest.mark.parametrize("kind", ["uniform", "correlated"])
-@pytest.mark.parametrize("packed", [False, True])
-def test_repeated_passes_bitwise_stable(dsv2, dsv2p, kind, packed):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_repeated_passes_bitwise_stable(dsv2_by_layout, kind, layout):
     """Many back-to-back passes on one workspace, per-slot and dedup alternating:
     every result bitwise equal to the first of its kind, the two kinds equal to
     summation order.  Data handed between workgroups (h, O, partial sums) that
     were not yet visible, or counters not reset between calls, would break it."""
-    dsv2 = dsv2p if packed else dsv2
+    dsv2 = dsv2_by_layout[layout]
     spec = dsv2.spec
     tr = routing.make_trace(spec, kind, 256, seed=31, p=0.5)
     ws = dsv2.dev.workspace(8)
@@ -320,35 +363,39 @@ def test_repeated_passes_bitwise_stable(dsv2, dsv2p, kind, packed):
         assert int(info[2].item()) == 0
 
 
-def test_packed_and_plain_agree(dsv2, dsv2p):
-    """The same passes with plain and packed W_down (the fused pass for n <= 8) agree to
-    fp32 summation order."""
+@pytest.mark.parametrize("other", ["packed", "tiled"])
+def test_layouts_agree_with_plain(dsv2_by_layout, other):
+    """The same passes with plain weights and with W_down packed or all three tiled
+    agree to fp32 summation order, routed experts alone and with the shared experts
+    in the call."""
+    dsv2 = dsv2_by_layout["plain"]
     spec = dsv2.spec
     tr = routing.make_trace(spec, "correlated", 256, seed=5, p=0.5)
     for n in (1, 2, 5, 8, 9):
         ids_h, w_h = routing.window(tr, 3 * n, n)
         x = synth.pass_x(spec, 5, 0, n, n)
-        say("plain vs packed n", n)
-        a = dsv2.run(x, ids_h, w_h)
-        b = dsv2p.run(x, ids_h, w_h)
-        _agree(a[0], b[0], "perslot plain/packed n=%d" % n)
-        _agree(a[1], b[1], "dedup plain/packed n=%d" % n)
+        sh = "fused" if n in (2, 9) else False
+        say("plain vs", other, "n", n, "shared", sh)
+        a = dsv2.run(x, ids_h, w_h, shared=sh)
+        b = dsv2_by_layout[other].run(x, ids_h, w_h, shared=sh)
+        _agree(a[0], b[0], "perslot plain/%s n=%d" % (other, n))
+        _agree(a[1], b[1], "dedup plain/%s n=%d" % (other, n))
 
 
-@pytest.mark.parametrize("packed", [False, True])
-def test_repeated_ids_count_as_often_as_they_appear(packed):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_repeated_ids_count_as_often_as_they_appear(layout):
     """An id repeated within a token (flagged MOE_E_IDS) counts as often as it appears in
     both kernels; with 8 tokens listing one expert 4 times its group has 32 slots, more
     than one 16-column tile."""
     spec = synth.layer_spec("tiny", N=20, m=4, d=128, d_ff=96, dtype="bf16")
-    dl = DeviceLayer(spec, 4, packed=packed)
+    dl = DeviceLayer(spec, 4, layout=layout)
     rng = np.random.default_rng(4)
     ids = np.stack([rng.choice(spec.N, spec.m, replace=False) for _ in range(8)]).astype(np.int32)
     ids[:, :] = 3
     ids[2, 1] = 7
     w = rng.random((8, spec.m)).astype(np.float32)
     x = synth.pass_x(spec, 4, 0, 0, 8)
-    say("repeated ids packed", packed)
+    say("repeated ids layout", layout)
     ys, yd, info = dl.run(x, ids, w)
     assert info[1] == efa._abi.MOE_E_IDS and info[0] == 2
     _agree(ys, yd, "repeated ids")

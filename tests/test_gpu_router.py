@@ -69,9 +69,10 @@ def test_router_ties_and_repeated_calls():
     assert torch.equal(a.ids, b.ids) and torch.equal(a.w, b.w) and torch.equal(a.logits, b.logits)
 
 
-def test_routed_pass_through_the_expert_kernels():
-    spec = synth.layer_spec("dsv2lite", N=16, m=4, d=256, d_ff=176, n_shared=0)
-    dl = DeviceLayer(spec, 12, packed=True)
+@pytest.mark.parametrize("layout,d_ff", [("packed", 176), ("tiled", 192)])
+def test_routed_pass_through_the_expert_kernels(layout, d_ff):
+    spec = synth.layer_spec("dsv2lite", N=16, m=4, d=256, d_ff=d_ff, n_shared=0)
+    dl = DeviceLayer(spec, 12, layout=layout)
     W = synth.router_weights(spec, 12)
     x = synth.pass_x(spec, 12, 0, 3, 7)
     say("routed pass")
