@@ -554,10 +554,16 @@ __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e,
 constexpr int kPF = 12;
 constexpr int kSL = 4;  // register mode: h staging loads in flight per thread
 
-// The per-slot kernel holds its registers to 4 waves per SIMD, so that a small
-// pass's gate/up and down work groups are all resident at once.
+// The per-slot kernel with down items in registers and one token tile holds its
+// registers to 4 waves per SIMD, so that a small pass's gate/up and down work
+// groups are all resident at once (a performance choice: every wait is on a lower
+// work-group id, so no wait depends on residency).  With streaming down items (long
+// d_ff) the work groups cannot all be resident anyway, and the cap (more work
+// groups per compute unit, each keeping less in flight) measured slower: a
+// Mixtral-shaped pass at n = 1 took 157 us against 140 us without it.  With 2 or 4
+// token tiles (shared experts, n > 16) the cap made the kernel spill.
 template <bool BF16, int MODE, int NT, int RB, bool KF, bool DPF, int LAY, bool SH>
-__global__ __launch_bounds__(kThreads, MODE == kPerSlot ? 4 : 1) void k_expert(Args a) {
+__global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF && NT == 1) ? 4 : 1) void k_expert(Args a) {
     using F = Fmt<BF16>;
     constexpr bool PK = LAY == kLayPacked, TL = LAY == kLayTiled;
     // ring depth in steps: operand registers per step are (2*RB + NT) for gate/up
