@@ -516,25 +516,61 @@ def extra_configs(args, torch, efa, synth, routing, ev, flush, stream, dedup_fit
     def run_all(fn, sets):
         for a in sets:
             assert fn(*a) == 0
+
+    # The same 48 launches also as HIP graphs (one capture per n and kernel over
+    # static id / weight buffers that each window is copied into), replayed on the
+    # bench stream: the serving form, with no host launch work per layer.
+    cap_stream = torch.cuda.Stream()  # default priority
+    grecs = []
     for n in range(1, 9):
         starts = routing.window_starts(T, n, reps + 1, seed=args.seed)
         y = torch.empty(n, spec.d, dtype=torch.float32, device="cuda")
+        yg = torch.empty(n, spec.d, dtype=torch.float32, device="cuda")
         x = xdev(spec, n, 1000 + n)
+        dev = [(torch.zeros(n, spec.m, dtype=torch.int32, device="cuda"),
+                torch.zeros(n, spec.m, dtype=torch.float32, device="cuda")) for _ in range(L)]
+        sets = argsets(n, x, dev, y)
+        graphs = {}
         for rp in range(reps + 1):
             win = [routing.window(traces[l], int(starts[rp]), n) for l in range(L)]
-            dev = [(torch.from_numpy(i).cuda(), torch.from_numpy(w).cuda()) for i, w in win]
+            for (di, dw), (i, w) in zip(dev, win):
+                di.copy_(torch.from_numpy(i))
+                dw.copy_(torch.from_numpy(w))
             U = [len(set(i.reshape(-1).tolist())) for i, _ in win]
-            sets = argsets(n, x, dev, y)
+            if not graphs:  # capture on the first window (the kernels' ids are read at run time)
+                torch.cuda.synchronize()
+                for kname, fn in (("slot", lib.moe_expert_perslot), ("dedup", lib.moe_expert_dedup)):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=cap_stream):
+                        gsets = [a[:6] + (vp(yg.data_ptr()),) + a[7:10] + (vp(cap_stream.cuda_stream),)
+                                 for a in sets]
+                        run_all(fn, gsets)
+                    graphs[kname] = g
+                torch.cuda.synchronize()
             ts = timed(lambda: run_all(lib.moe_expert_perslot, sets))
+            tgs = timed(lambda: graphs["slot"].replay())
+            assert torch.equal(y, yg), "graph replay differs from the eager launches (per-slot)"
             td = timed(lambda: run_all(lib.moe_expert_dedup, sets))
+            tgd = timed(lambda: graphs["dedup"].replay())
+            assert torch.equal(y, yg), "graph replay differs from the eager launches (dedup)"
             if rp > 0:
                 recs.append(dict(n=n, U=sum(U) / L, bytes_slot=L * n * spec.m * w_exp, bytes_dedup=sum(U) * w_exp,
                                  t_slot_ms=ts, t_dedup_ms=td))
+                grecs.append(dict(n=n, slot_eager_us=ts * 1e3, slot_graph_us=tgs * 1e3, dedup_eager_us=td * 1e3,
+                                  dedup_graph_us=tgd * 1e3))
+        del graphs
     qrows = per_n_rows(recs, range(1, 9))
     out["qwen3_x48"] = {"workload": "qwen3-shaped layer x48 back to back per pass (N=128, m=8, d=2048, d_ff=768, "
                                     "bf16), zipf(s=1.1) routing per layer, %d passes per n" % reps,
                         "per_n": strip_bytes(qrows), "crossover": crossover_of(qrows),
-                        "step_model": step_model_section(efa, spec, qrows, [], layers=L)}
+                        "step_model": step_model_section(efa, spec, qrows, [], layers=L),
+                        "hip_graph": {"what": "the 48 launches of a pass captured once per n and kernel, replayed "
+                                              "after each window is copied into the captured id/weight buffers; "
+                                              "us per pass of 48 layers, median of %d windows" % reps,
+                                      "per_n": [{k: (round(float(np.median([r[k] for r in grecs if r["n"] == n])), 1)
+                                                     if k != "n" else n)
+                                                 for k in ("n", "slot_eager_us", "slot_graph_us", "dedup_eager_us",
+                                                           "dedup_graph_us")} for n in range(1, 9)]}}
 
     # ---- 32-node draft tree on one Qwen3-shaped layer ----
     tl = layers[0]

@@ -18,7 +18,7 @@ import synth
 from synth import routing
 from synth.device import to_torch
 
-from .gpu_cases import LAYOUTS, SUMMATION_TOL, DeviceLayer, assert_close, errors, say, step_multiple
+from .gpu_cases import LAYOUTS, SUMMATION_TOL, SYNC_BYTES, DeviceLayer, assert_close, errors, say, step_multiple
 
 pytestmark = pytest.mark.gpu
 
@@ -427,3 +427,49 @@ def test_expert_auto_runs_the_kernel_the_crossover_names():
             want = efa.MOE_KIND_DEDUP if (c > 0 and n >= c) else efa.MOE_KIND_SLOT
             assert kind == want
             assert torch.equal(y, yd if want == efa.MOE_KIND_DEDUP else ys)
+
+
+def test_hip_graph_replays_equal_eager_calls():
+    """Both kernels captured in a HIP graph over static id / weight buffers, replayed
+    three times with eager kernel calls, torch work and new windows copied in between:
+    every replay bitwise equal to the eager call on the same window (the kernels issue
+    no memset; the workspace counters are reset by the kernels themselves)."""
+    spec = synth.layer_spec("dsv2lite", N=16, m=4, d=256, d_ff=192, n_shared=2)
+    dl = DeviceLayer(spec, 41, with_shared=True, layout="tiled")
+    layer = dl.fused
+    n = 6
+    tr = routing.make_trace(spec, "correlated", 64, seed=41, p=0.5)
+    x = to_torch(synth.pass_x(spec, 41, 0, 0, n))
+    ids = torch.zeros(n, spec.m, dtype=torch.int32, device="cuda")
+    w = torch.zeros(n, spec.m, dtype=torch.float32, device="cuda")
+    ws_g, ws_e = layer.workspace(n), layer.workspace(n)
+    yg = {k: torch.zeros(n, spec.d, dtype=torch.float32, device="cuda") for k in ("slot", "dedup")}
+    fns = {"slot": efa.expert_perslot, "dedup": efa.expert_dedup}
+    i0, w0 = routing.window(tr, 0, n)
+    ids.copy_(torch.from_numpy(i0))
+    w.copy_(torch.from_numpy(w0))
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()  # default priority
+    graphs = {}
+    for k, fn in fns.items():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            fn(layer, x, ids, w, y=yg[k], ws=ws_g, stream=cap)
+        graphs[k] = g
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ih, wh = routing.window(tr, 5 + 7 * rep, n)
+        ids.copy_(torch.from_numpy(ih))
+        w.copy_(torch.from_numpy(wh))
+        for k, fn in fns.items():
+            say("graph replay", rep, k)
+            graphs[k].replay()
+            torch.cuda.synchronize()
+            ye = fn(layer, x, ids, w, ws=ws_e)  # eager, own workspace
+            _ = (ye * 2.0).sum()                # unrelated torch work between replays
+            torch.cuda.synchronize()
+            assert torch.equal(yg[k], ye), (rep, k)
+        ref = dl.oracle_y(synth.pass_x(spec, 41, 0, 0, n), ih, wh, shared=True)
+        assert_close(yg["slot"].cpu().numpy(), ref, "graph slot rep %d" % rep)
+        assert_close(yg["dedup"].cpu().numpy(), ref, "graph dedup rep %d" % rep)
+    assert np.all(ws_g[:SYNC_BYTES].cpu().numpy() == 0)
