@@ -12,7 +12,9 @@
 //   * a "unit" is a slot (per-slot) or a distinct expert with its group of slots
 //     (deduplicating).  Grid = [gate/up items][down items], each item a 16-row
 //     output tile of one unit, owned by a workgroup of 4 wave64s that split the
-//     contraction dimension K into four contiguous ranges.
+//     contraction dimension K into four contiguous ranges, or, with tiled weights
+//     (blocks of 16 rows x one K step, see TSteps), take every fourth step so that
+//     at each step they read adjacent blocks.
 //   * the contraction runs on MFMA (bf16 16x16x32, or fp32 16x16x4): the weight
 //     tile is the A operand taken straight from buffer loads (16 B per lane, row
 //     lane%16, k-group lane/16); the token activations are the B operand, 16
@@ -228,9 +230,9 @@ __device__ __forceinline__ int atomic_load_agent(const int32_t* p) {
 }
 
 struct Args {
-    const char* wg;      // W_gate [N][d_ff][d]
-    const char* wu;      // W_up   [N][d_ff][d]
-    const char* wd;      // W_down [N][d][d_ff] (or packed)
+    const char* wg;      // W_gate [N][d_ff][d] (or tiled)
+    const char* wu;      // W_up   [N][d_ff][d] (or tiled)
+    const char* wd;      // W_down [N][d][d_ff] (or packed, or tiled)
     const char* wgs;     // always-on (shared) experts: W_gate [n_shared][d_ff][d], or null
     const char* wus;     // W_up [n_shared][d_ff][d]
     const char* wds;     // W_down [n_shared][d][d_ff], layout as wd
