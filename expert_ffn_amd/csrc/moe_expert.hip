@@ -1303,6 +1303,9 @@ struct Plan {
     size_t h_off, o_off, sync_off, total;
 };
 
+// work groups per compute unit at once: the per-slot register-mode kernel's launch
+// bound, and what the deduplicating kernel's registers allow
+constexpr int kResidentSlot = 4, kResidentDedup = 3;
 constexpr int kHsBudget = 24 * 1024;  // LDS bytes for staged h (down items in register mode)
 // per-slot passes with shared experts: LDS for the shared experts' h chunks
 constexpr int kHsBudgetShared = 12 * 1024;
@@ -1321,34 +1324,8 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     p.nt = (!wide || n <= 16) ? 1 : (n <= 32 ? 2 : 4);
     p.rb = p.nt == 4 ? 1 : 2;  // rows per item = 16 * rb; row blocks x token tiles <= 4
     p.T1 = (d->d_ff + kTile * p.rb - 1) / (kTile * p.rb);
-    // register mode when a wave's share of the down contraction fits kPF steps
     const bool bf = d->dtype == MOE_BF16;
-    const int es = bf ? 2 : 4, step = 64 / es;
-    const int s2 = (d->d_ff + step - 1) / step;
-    const int per_tok = (d->d_ff * es + 16) * (bf ? 2 : 1);  // staged bytes per token
-    const int gmax = kind == MOE_KIND_SLOT ? 1 : n;  // routed group size is at most n (valid ids)
-    // (and only when one LDS chunk of at most 16 tokens, one MFMA column tile,
-    // holds a whole group: several chunks would serialise their h loads and O
-    // stores).  A per-slot pass with shared experts stages their n tokens in
-    // chunks of what kHsBudgetShared holds.
-    const bool steps_fit = (s2 + kWaves - 1) / kWaves <= kPF;
-    if (kind == MOE_KIND_SLOT && d->n_shared > 0) {
-        const int cap = (int)std::max<int64_t>(1, kHsBudgetShared / per_tok);
-        p.dpf = steps_fit && (int64_t)per_tok <= kHsBudget;
-        p.gl = p.dpf ? std::min(n, std::min(cap, 16)) : 0;
-    } else {
-        p.dpf = steps_fit && gmax <= 16 && (int64_t)per_tok * gmax <= kHsBudget;
-        p.gl = p.dpf ? gmax : 0;
-    }
-    p.lds = p.dpf ? (size_t)p.gl * per_tok : 0;
-    const int rb2 = p.dpf ? 1 : p.rb;
-    p.T2 = (d->d_model + kTile * rb2 - 1) / (kTile * rb2);
-    // Streaming down items (not register mode) each stream their rows' W_down after
-    // the wait, at what one work group keeps in flight; with fewer than 4 items per
-    // compute unit the d_ff contraction of each (unit, row tile) is cut into ks
-    // parts, one item each, summed in the combine.
-    const int64_t ditems = (int64_t)p.units * p.T2;
-    p.ks = p.dpf ? 1 : (int)std::min<int64_t>(kMaxKs, std::max<int64_t>(1, (4 * kCUs + ditems - 1) / ditems));
+    const int es = bf ? 2 : 4, step = 64 / es;  // bytes per element, elements per K step
     // Gate/up work is cut into kCUs equal shares when there are between half and
     // twice as many tiles as compute units: then no compute unit holds two tiles
     // while another holds one.  With fewer tiles than half the compute units (a
@@ -1363,6 +1340,40 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     const bool few = tiles * 2 < kCUs && p.S1 >= 2;
     const bool split = ((tiles * 2 >= kCUs && tiles < 2 * kCUs) || few) && part_bytes <= (64ll << 20);
     p.g1 = !split ? (int)tiles : (few ? (int)(2 * tiles) : kCUs);
+    // Down items in register mode: when a wave's share of the down contraction fits
+    // kPF steps, and one LDS chunk of at most 16 tokens (one MFMA column tile) holds a
+    // whole group (several chunks would serialise their h loads and O stores; a
+    // per-slot pass with shared experts stages their n tokens in chunks of what
+    // kHsBudgetShared holds), and the pass's work groups (gate/up, then register-mode
+    // down items) fill at most 11/4 rounds of what the compute units hold at once.
+    // Register-mode items prefetch their W_down while they wait, which pays for those
+    // resident during gate/up; items dispatched after it run in rounds of short,
+    // latency-bound work, where streaming items (twice the rows, a load ring) do
+    // better.  Same-box: every pass measured at 2.7 rounds or fewer was faster in
+    // register mode, every one at 3 or more faster streaming.
+    const int s2 = (d->d_ff + step - 1) / step;
+    const int per_tok = (d->d_ff * es + 16) * (bf ? 2 : 1);  // staged bytes per token
+    const int gmax = kind == MOE_KIND_SLOT ? 1 : n;  // routed group size is at most n (valid ids)
+    const int64_t resident = (int64_t)kCUs * (kind == MOE_KIND_SLOT ? kResidentSlot : kResidentDedup);
+    const int64_t dpf_items = (int64_t)p.units * ((d->d_model + kTile - 1) / kTile);
+    const bool reg_ok = (s2 + kWaves - 1) / kWaves <= kPF && 4 * (p.g1 + dpf_items) <= 11 * resident;
+    if (kind == MOE_KIND_SLOT && d->n_shared > 0) {
+        const int cap = (int)std::max<int64_t>(1, kHsBudgetShared / per_tok);
+        p.dpf = reg_ok && (int64_t)per_tok <= kHsBudget;
+        p.gl = p.dpf ? std::min(n, std::min(cap, 16)) : 0;
+    } else {
+        p.dpf = reg_ok && gmax <= 16 && (int64_t)per_tok * gmax <= kHsBudget;
+        p.gl = p.dpf ? gmax : 0;
+    }
+    p.lds = p.dpf ? (size_t)p.gl * per_tok : 0;
+    const int rb2 = p.dpf ? 1 : p.rb;
+    p.T2 = (d->d_model + kTile * rb2 - 1) / (kTile * rb2);
+    // Streaming down items (not register mode) each stream their rows' W_down after
+    // the wait, at what one work group keeps in flight; with fewer than 4 items per
+    // compute unit the d_ff contraction of each (unit, row tile) is cut into ks
+    // parts, one item each, summed in the combine.
+    const int64_t ditems = (int64_t)p.units * p.T2;
+    p.ks = p.dpf ? 1 : (int)std::min<int64_t>(kMaxKs, std::max<int64_t>(1, (4 * kCUs + ditems - 1) / ditems));
     p.sync_off = 0;
     p.h_off = (size_t)kSyncWords * 4;
     p.o_off = p.h_off + align_up((size_t)p.nslot * d->d_ff * 4);
