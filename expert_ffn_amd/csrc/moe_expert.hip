@@ -551,8 +551,10 @@ __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e,
 // ---------------------------------------------------------------------------
 // The fused expert operation.
 // ---------------------------------------------------------------------------
-// Down items hold all of their W_down rows in registers (DPF) when a wave's share
-// of the contraction is at most kPF steps.
+// Down items hold all of their W_down rows in registers (register mode, DPF > 0)
+// when a wave's share of the contraction is at most kPF steps: 16 rows (DPF = 1), or,
+// when it is at most kPF / 2 steps, 32 rows in the same registers (DPF = 2: half as
+// many down items, so more of them are resident while gate/up runs).
 constexpr int kPF = 12;
 constexpr int kSL = 4;  // register mode: h staging loads in flight per thread
 
@@ -564,8 +566,8 @@ constexpr int kSL = 4;  // register mode: h staging loads in flight per thread
 // groups per compute unit, each keeping less in flight) measured slower: a
 // Mixtral-shaped pass at n = 1 took 157 us against 140 us without it.  With 2 or 4
 // token tiles (shared experts, n > 16) the cap made the kernel spill.
-template <bool BF16, int MODE, int NT, int RB, bool KF, bool DPF, int LAY, bool SH>
-__global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF && NT == 1) ? 4 : 1) void k_expert(Args a) {
+template <bool BF16, int MODE, int NT, int RB, bool KF, int DPF, int LAY, bool SH>
+__global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) ? 4 : 1) void k_expert(Args a) {
     using F = Fmt<BF16>;
     constexpr bool PK = LAY == kLayPacked, TL = LAY == kLayTiled;
     // ring depth in steps: operand registers per step are (2*RB + NT) for gate/up
@@ -574,7 +576,8 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF && NT == 1) ? 4 
     constexpr int H = P / 2;  // half ring
     // down items: one row block in register mode (the W_down rows a wave holds),
     // else RB like the gate/up items
-    constexpr int RB2 = DPF ? 1 : RB;
+    constexpr int RB2 = DPF == 2 ? 2 : (DPF == 1 ? 1 : RB);
+    constexpr int PF = DPF == 2 ? kPF / 2 : kPF;  // register mode: W_down steps a wave holds
     constexpr int RT2 = kTile * RB2;
     __shared__ Smem<NT * RB> sm;
     __shared__ int s_last;
@@ -702,16 +705,16 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF && NT == 1) ? 4 
                        : PK ? bload2<0>(rd, pst.vofs(lrow[rb], j), pst.sofs(j))
                             : bload2<0>(rd, st.vofs(lrow[rb], j), st.sofs(j));
             };
-            if constexpr (DPF) {
+            if constexpr (DPF > 0) {
                 // All of this wave's W_down rows go to registers before the wait, so
                 // they stream from HBM while gate/up items still run.  After the
                 // wait, h is staged in LDS `gl` tokens at a time (one cooperative
                 // sc1 load per chunk) and the products run from registers and LDS,
                 // for any group size with one read of the weights.
                 extern __shared__ __align__(16) char hs[];  // [gl][hi row, lo row], padded rows
-                u32x4 pa[kPF][RB2];
+                u32x4 pa[PF][RB2];
 #pragma unroll
-                for (int i = 0; i < kPF; ++i)
+                for (int i = 0; i < PF; ++i)
 #pragma unroll
                     for (int rb = 0; rb < RB2; ++rb) pa[i][rb] = wload(rb, i);
                 if (tid == 0 && !wait_count(hcnt, a.T1) && a.info) a.info[2] = MOE_E_HIP;
@@ -751,7 +754,7 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF && NT == 1) ? 4 
 #pragma unroll
                     for (int rb = 0; rb < RB2; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int i = 0; i < kPF; ++i) {
+                    for (int i = 0; i < PF; ++i) {
                         if (i < ns) {
                             const int k = st.step(i) * F::kStep + q * F::kPer;
                             const bool ok = col_ok && k < a.d_ff;
@@ -1297,7 +1300,7 @@ struct Plan {
     int units, units_r, nslot, T1, T2, nt, rb, ks;
     int g1, S1;  // gate/up work groups, K steps per gate/up tile
     size_t part_off;
-    bool dpf;    // down items in register mode
+    int dpf;     // down items: 0 streaming, 1 register mode (16 rows), 2 register mode (32 rows)
     int gl;      // register mode: tokens of h staged in LDS at a time
     size_t lds;  // register mode: dynamic LDS bytes
     size_t h_off, o_off, sync_off, total;
@@ -1355,18 +1358,21 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     const int per_tok = (d->d_ff * es + 16) * (bf ? 2 : 1);  // staged bytes per token
     const int gmax = kind == MOE_KIND_SLOT ? 1 : n;  // routed group size is at most n (valid ids)
     const int64_t resident = (int64_t)kCUs * (kind == MOE_KIND_SLOT ? kResidentSlot : kResidentDedup);
-    const int64_t dpf_items = (int64_t)p.units * ((d->d_model + kTile - 1) / kTile);
-    const bool reg_ok = (s2 + kWaves - 1) / kWaves <= kPF && 4 * (p.g1 + dpf_items) <= 11 * resident;
+    const int wsteps = (s2 + kWaves - 1) / kWaves;  // a wave's share of the down contraction
+    const bool kf = d->d_model % step == 0 && d->d_ff % step == 0;
+    const int reg_rows = (kf && wsteps <= kPF / 2) ? 2 : 1;  // row blocks of a register-mode item
+    const int64_t dpf_items = (int64_t)p.units * ((d->d_model + kTile * reg_rows - 1) / (kTile * reg_rows));
+    const bool reg_ok = wsteps <= kPF && 4 * (p.g1 + dpf_items) <= 11 * resident;
     if (kind == MOE_KIND_SLOT && d->n_shared > 0) {
         const int cap = (int)std::max<int64_t>(1, kHsBudgetShared / per_tok);
-        p.dpf = reg_ok && (int64_t)per_tok <= kHsBudget;
+        p.dpf = (reg_ok && (int64_t)per_tok <= kHsBudget) ? reg_rows : 0;
         p.gl = p.dpf ? std::min(n, std::min(cap, 16)) : 0;
     } else {
-        p.dpf = reg_ok && gmax <= 16 && (int64_t)per_tok * gmax <= kHsBudget;
+        p.dpf = (reg_ok && gmax <= 16 && (int64_t)per_tok * gmax <= kHsBudget) ? reg_rows : 0;
         p.gl = p.dpf ? gmax : 0;
     }
     p.lds = p.dpf ? (size_t)p.gl * per_tok : 0;
-    const int rb2 = p.dpf ? 1 : p.rb;
+    const int rb2 = p.dpf ? p.dpf : p.rb;
     p.T2 = (d->d_model + kTile * rb2 - 1) / (kTile * rb2);
     // Streaming down items (not register mode) each stream their rows' W_down after
     // the wait, at what one work group keeps in flight; with fewer than 4 items per
@@ -1387,18 +1393,21 @@ void launch_lay(const Args& args, const Plan& p, int grid, hipStream_t st) {
     constexpr int step = Fmt<BF16>::kStep;
     // tiled weights have K a multiple of the step in both contractions (check_desc)
     const bool kf = LAY == kLayTiled || (args.d % step == 0 && args.d_ff % step == 0);
-    if (kf && p.dpf)
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, true, LAY, SH>), dim3(grid), dim3(kThreads), p.lds, st,
+    if (kf && p.dpf == 2)  // (32-row register mode is planned only for whole steps)
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, 2, LAY, SH>), dim3(grid), dim3(kThreads), p.lds, st,
+                           args);
+    else if (kf && p.dpf == 1)
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, 1, LAY, SH>), dim3(grid), dim3(kThreads), p.lds, st,
                            args);
     else if (kf)
-        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, false, LAY, SH>), dim3(grid), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, 0, LAY, SH>), dim3(grid), dim3(kThreads), 0, st,
                            args);
     else if constexpr (LAY != kLayTiled) {
         if (p.dpf)
-            hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, true, LAY, SH>), dim3(grid), dim3(kThreads), p.lds,
+            hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, 1, LAY, SH>), dim3(grid), dim3(kThreads), p.lds,
                                st, args);
         else
-            hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, false, LAY, SH>), dim3(grid), dim3(kThreads), 0, st,
+            hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, false, 0, LAY, SH>), dim3(grid), dim3(kThreads), 0, st,
                                args);
     }
 }
