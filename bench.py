@@ -82,7 +82,8 @@ def load_layout(layer):
 
 def source_hash():
     h = hashlib.sha256()
-    for p in ("expert_ffn_amd/csrc/moe_expert.hip",):
+    for p in ("expert_ffn_amd/csrc/expert_kernel.h", "expert_ffn_amd/csrc/expert_launch.hip",
+              "expert_ffn_amd/csrc/moe_expert.hip"):
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 

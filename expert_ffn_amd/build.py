@@ -5,6 +5,7 @@
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -30,16 +31,32 @@ def _run(cmd):
         sys.stderr.write(out + "\n")
 
 
-def build(verbose=False):
+def _variant_objects():
+    """(source, object, defines) of the fused kernel's variant groups."""
+    src = os.path.join(CSRC, "expert_launch.hip")
+    out = []
+    for b in (0, 1):
+        for m in (0, 1):
+            for s in (0, 1):
+                out.append((src, os.path.join(BUILD, "expert_launch_%d%d%d.o" % (b, m, s)),
+                            ["-DMOE_K_BF16=%d" % b, "-DMOE_K_MODE=%d" % m, "-DMOE_K_SH=%d" % s]))
+    return out
+
+
+def build(verbose=False, jobs=None):
+    """Compile every translation unit (in parallel, `jobs` at a time; default: the
+    CPU count, at most 8) and link the shared library."""
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
-    hip_src = os.path.join(CSRC, "moe_expert.hip")
-    o1 = os.path.join(BUILD, "moe_expert.o")
-    _run([HIPCC, "--offload-arch=" + ARCH, *COMMON, *DEVICE_FLAGS, "-c", hip_src, "-o", o1])
-    objs.append(o1)
+    hip = [(os.path.join(CSRC, "moe_expert.hip"), os.path.join(BUILD, "moe_expert.o"), [])] + _variant_objects()
+    cmds = [[HIPCC, "--offload-arch=" + ARCH, *COMMON, *DEVICE_FLAGS, *defs, "-c", src, "-o", obj]
+            for src, obj, defs in hip]
     o2 = os.path.join(BUILD, "host_model.o")
-    _run([HIPCC, *COMMON, "-x", "c++", "-c", os.path.join(CSRC, "host_model.cpp"), "-o", o2])
-    objs.append(o2)
+    cmds.append([HIPCC, *COMMON, "-x", "c++", "-c", os.path.join(CSRC, "host_model.cpp"), "-o", o2])
+    jobs = jobs or min(8, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        for f in [pool.submit(_run, c) for c in cmds]:
+            f.result()
+    objs = [obj for _, obj, _ in hip] + [o2]
     tmp = SO + ".tmp%d" % os.getpid()
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, SO)
