@@ -573,9 +573,13 @@ constexpr int kSL = 4;  // register mode: h staging loads in flight per thread
 // d_ff) the work groups cannot all be resident anyway, and the cap (more work
 // groups per compute unit, each keeping less in flight) measured slower: a
 // Mixtral-shaped pass at n = 1 took 157 us against 140 us without it.  With 2 or 4
-// token tiles (shared experts, n > 16) the cap made the kernel spill.
+// token tiles (shared experts, n > 16) the cap made the kernel spill.  With 2 token
+// tiles (passes of 17..32 tokens) the kernel is held to 3 waves per SIMD (3-4 VGPRs
+// spill): the latency-bound down items of a 32-token tree pass overlap more, 6 %
+// faster than at the 2 waves its registers would otherwise allow.
 template <bool BF16, int MODE, int NT, int RB, bool KF, int DPF, int LAY, bool SH>
-__global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) ? 4 : 1) void k_expert(Args a) {
+__global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) ? 4 : (NT == 2 ? 3 : 1)) void k_expert(
+    Args a) {
     using F = Fmt<BF16>;
     constexpr bool PK = LAY == kLayPacked, TL = LAY == kLayTiled;
     // ring depth in steps: operand registers per step are (2*RB + NT) for gate/up
