@@ -298,3 +298,23 @@ def test_expert_auto_rejects_negative_crossover():
     # a bad descriptor is reported by the kernel it would run, before any launch
     assert L.moe_expert_auto(ctypes.byref(_desc(m=0)), ctypes.byref(W), fake, fake, fake, 4, fake, None, fake,
                              1 << 30, 2, None, None) == _abi.MOE_E_INVAL
+
+
+def test_c_program_uses_the_abi(tmp_path):
+    """The header compiles as C99 (-Wall -Werror) and a C program linked against the
+    library gets host results equal to the Python binding's, and validation errors
+    before any launch (no GPU needed)."""
+    exe = str(tmp_path / "abi_host")
+    lib_dir = os.path.dirname(_abi.SO_PATH)
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "c", "abi_host.c"), "-o", exe, "-L", lib_dir, "-lmoe_expert",
+           "-Wl,-rpath," + lib_dir]
+    import subprocess
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout
+    r = subprocess.run([exe], stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    out = dict(l.split(" ", 1) for l in r.stdout.strip().splitlines())
+    assert out["failures"] == "0"
+    d = _desc(N=64, m=6, d_model=2048, d_ff=1408, dtype=_abi.MOE_BF16)
+    assert int(out["workspace_slot_n8"]) == _abi.lib().moe_workspace_bytes(ctypes.byref(d), 8, 0)
