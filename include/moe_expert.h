@@ -84,7 +84,8 @@ typedef struct {
     uint32_t flags;   /* MOE_FLAG_* */
     int32_t n_shared; /* always-on (shared) experts computed in the same call,
                          0 .. MOE_MAX_SHARED; 0 = none.  Same d_model, d_ff, dtype
-                         and W_down layout as the routed experts. */
+                         and weight layout (plain, W_down packed, or all three
+                         tiled, as flags say) as the routed experts. */
 } moe_layer_desc;
 
 /* Device pointers, caller-owned, 16-byte aligned, layouts as above.  The shared
