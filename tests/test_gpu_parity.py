@@ -473,3 +473,34 @@ def test_hip_graph_replays_equal_eager_calls():
         assert_close(yg["slot"].cpu().numpy(), ref, "graph slot rep %d" % rep)
         assert_close(yg["dedup"].cpu().numpy(), ref, "graph dedup rep %d" % rep)
     assert np.all(ws_g[:SYNC_BYTES].cpu().numpy() == 0)
+
+
+@pytest.mark.parametrize("layout", ["plain", "tiled"])
+def test_limits_experts_slots_width(layout):
+    """At the limits of the boundary: N = 1024 experts with ids up to 1023 and
+    n*m = 256 slots (n = 64); d_model = 16384, the widest layer (1024 down row tiles,
+    every arrival counter line in use); m = N (every token selects every expert)."""
+    rng = np.random.default_rng(9)
+    # N = 1024, n = 64, m = 4: slots at the unit limit, ids drawn from the top of the range
+    spec = synth.layer_spec("tiny", N=1024, m=4, d=64, d_ff=64, dtype="bf16", sigma=0.05)
+    dl = DeviceLayer(spec, 9, layout=layout)
+    ids = np.stack([rng.choice(np.arange(960, 1024), 4, replace=False) for _ in range(64)]).astype(np.int32)
+    ids[0] = [1023, 0, 512, 1022]
+    w = rng.random((64, 4)).astype(np.float32)
+    say("limits N=1024 n=64", layout)
+    _compare(dl, synth.pass_x(spec, 9, 0, 0, 64), ids, w, "N=1024 n=64")
+    # d_model = 16384
+    spec = synth.layer_spec("tiny", N=3, m=2, d=16384, d_ff=64, dtype="bf16", sigma=0.02)
+    dl = DeviceLayer(spec, 10, layout=layout)
+    for n in (1, 3):
+        ids = np.stack([rng.choice(3, 2, replace=False) for _ in range(n)]).astype(np.int32)
+        w = rng.random((n, 2)).astype(np.float32)
+        say("limits d=16384 n", n, layout)
+        _compare(dl, synth.pass_x(spec, 10, 0, n, n), ids, w, "d=16384 n=%d" % n)
+    # m = N
+    spec = synth.layer_spec("tiny", N=4, m=4, d=96, d_ff=128, dtype="bf16", sigma=0.05)
+    dl = DeviceLayer(spec, 11, layout=layout)
+    ids = np.stack([rng.permutation(4) for _ in range(8)]).astype(np.int32)
+    w = rng.random((8, 4)).astype(np.float32)
+    say("limits m=N", layout)
+    _compare(dl, synth.pass_x(spec, 11, 0, 0, 8), ids, w, "m=N")
