@@ -117,19 +117,21 @@ def _counter_rows(path):
     return list(csv.DictReader(open(path)))
 
 
-def traffic_from(fetch_csv, write_csv, config):
-    """HBM bytes per per-slot launch from two counter runs of `--pmc-pass`.
+def traffic_from(fetch_csv, write_csv, config, kernel="slot"):
+    """HBM bytes per launch of one kernel ("slot" or "dedup", told apart by the
+    kernel's mode template argument) from two counter runs of `--pmc-pass`.
 
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
     counter reads for the run's device copy of COPY_BYTES (read and written once),
-    then averaged over the per-slot launches, like the achieved figure."""
+    then averaged over the kernel's launches, like the achieved figure."""
+    tag = "k_expert<true, %d," % (0 if kernel == "slot" else 1)
     out = {}
     for name, path in (("fetch", fetch_csv), ("write", write_csv)):
         rows = _counter_rows(path)
         copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         cal = max(copy)  # the 256 MiB device copy is the largest copy of the run
         factor = COPY_BYTES / (cal * 1024.0)
-        ke = [float(r["Counter_Value"]) for r in rows if "k_expert" in r["Kernel_Name"]]
+        ke = [float(r["Counter_Value"]) for r in rows if tag in r["Kernel_Name"]]
         out[name] = dict(copy_kib=cal, factor=factor, kernel_kib=ke, bytes=[v * 1024.0 * factor for v in ke])
     n = len(out["fetch"]["bytes"])
     assert n == len(out["write"]["bytes"]) and n > 0
@@ -140,7 +142,9 @@ def traffic_from(fetch_csv, write_csv, config):
 def write_traffic_summary(fetch_csv, write_csv, config, pass_json):
     info = [json.loads(l) for l in open(pass_json) if l.startswith('{"pmc_pass"')][-1]
     out, per_launch = traffic_from(fetch_csv, write_csv, config)
-    alg = [p["bytes"] for p in info["pmc_pass"]]
+    slot_pass = [p for p in info["pmc_pass"] if p.get("kernel", "slot") == "slot"]
+    dedup_pass = [p for p in info["pmc_pass"] if p.get("kernel") == "dedup"]
+    alg = [p["bytes"] for p in slot_pass]
     n = len(alg)
     assert n == len(out["fetch"]["bytes"])
     rec = {"kernel": "k_expert per-slot", "config": config, "launches": n,
@@ -158,12 +162,29 @@ def write_traffic_summary(fetch_csv, write_csv, config, pass_json):
                                                              out["write"]["factor"]),
              "", "| routing | n | algorithmic MB | fetched MB (scaled) | written MB (scaled) | fetched / algorithmic |",
              "|---|---|---|---|---|---|"]
-    for i, p in enumerate(info["pmc_pass"]):
+    for i, p in enumerate(slot_pass):
         fb, wb = out["fetch"]["bytes"][i], out["write"]["bytes"][i]
         lines.append("| %s | %d | %.1f | %.1f | %.2f | %.3f |" % (p["kind"], p["n"], p["bytes"] / 1e6, fb / 1e6,
                                                                  wb / 1e6, fb / p["bytes"]))
     lines += ["", "Per launch (average over the %d launches): %.1f MB counted, %.1f MB algorithmic." % (
-        n, per_launch / 1e6, sum(alg) / n / 1e6), "", "traffic-json: " + json.dumps(rec)]
+        n, per_launch / 1e6, sum(alg) / n / 1e6)]
+    if dedup_pass:
+        dout, dper = traffic_from(fetch_csv, write_csv, config, kernel="dedup")
+        assert len(dedup_pass) == len(dout["fetch"]["bytes"])
+        lines += ["", "The deduplicating kernel on the same passes: U distinct experts, each to be read once "
+                  "(algorithmic U w).", "",
+                  "| routing | n | U | algorithmic MB | fetched MB (scaled) | written MB (scaled) | "
+                  "fetched / algorithmic |", "|---|---|---|---|---|---|---|"]
+        for i, p in enumerate(dedup_pass):
+            fb, wb = dout["fetch"]["bytes"][i], dout["write"]["bytes"][i]
+            lines.append("| %s | %d | %d | %.1f | %.1f | %.2f | %.3f |" % (
+                p["kind"], p["n"], p["U"], p["bytes"] / 1e6, fb / 1e6, wb / 1e6, fb / p["bytes"]))
+        dalg = sum(p["bytes"] for p in dedup_pass) / len(dedup_pass)
+        lines += ["", "Per dedup launch (average over the %d launches): %.1f MB counted, %.1f MB algorithmic." % (
+            len(dedup_pass), dper / 1e6, dalg / 1e6)]
+        rec["dedup_bytes_per_launch"] = round(dper, 1)
+        rec["dedup_algorithmic_bytes_per_launch"] = round(dalg, 1)
+    lines += ["", "traffic-json: " + json.dumps(rec)]
     path = os.path.join(ROOT, "profiles", "traffic_k_expert_perslot_%s.md" % config)
     open(path, "w").write("\n".join(lines) + "\n")
     print(path)
@@ -737,13 +758,18 @@ def main():
         # Counter run: the flush (a plain read of SCRUB_BYTES) and a device copy
         # (COPY_BYTES read and written) calibrate FETCH_SIZE and WRITE_SIZE; the
         # per-slot launches in between are the ones the bench times.
+        # (then the deduplicating kernel on the same passes: it reads each of the U
+        # distinct experts once)
         order = []
-        for kind, _ in kinds:
-            for n in nvals:
-                p = passes[(kind, n, args.warmup)]
-                flush()
-                efa.expert_perslot(layer, p["x"], p["ids"], p["w"], y=ys[n], ws=ws, stream=stream)
-                order.append(dict(kind=kind, n=n, bytes=n * spec.m * w_exp))
+        for kname, fn in (("slot", efa.expert_perslot), ("dedup", efa.expert_dedup)):
+            for kind, _ in kinds:
+                for n in nvals:
+                    p = passes[(kind, n, args.warmup)]
+                    U = len(set(p["ids"].cpu().numpy().ravel().tolist()))
+                    flush()
+                    fn(layer, p["x"], p["ids"], p["w"], y=ys[n], ws=ws, stream=stream)
+                    order.append(dict(kernel=kname, kind=kind, n=n, U=U,
+                                      bytes=(n * spec.m if kname == "slot" else U) * w_exp))
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
