@@ -112,6 +112,19 @@ PROF_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof -o run --output
             "python3 bench.py --no-extras > gpurun_out/prof_bench.json")
 
 
+def progress(msg):
+    """A stage of the run has finished (stderr; stdout carries only the JSON line)."""
+    print("[bench] %s" % msg, file=sys.stderr, flush=True)
+
+
+def prof_cmd(config):
+    """The kernel-trace command whose summary profiles/k_expert_<config>_n1-8.md holds."""
+    if config == "dsv2lite":
+        return PROF_CMD
+    return ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_%s -o run --output-format csv -- "
+            "python3 bench.py --config %s --no-extras > gpurun_out/prof_bench_%s.json" % (config, config, config))
+
+
 def _counter_rows(path):
     import csv
     return list(csv.DictReader(open(path)))
@@ -218,7 +231,7 @@ def write_profile_summary(prof_dir, bench_json, config):
         d[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000)
     b = [json.loads(l) for l in open(bench_json) if l.startswith('{"metric"')][-1]
     lines = ["# k_expert (per-slot and deduplicating), %s-shaped layer, n = 1..8, uniform + correlated routing" % config,
-             "", "Command (from the repository root, one MI355X):", "", "```", PROF_CMD, "```", "",
+             "", "Command (from the repository root, one MI355X):", "", "```", prof_cmd(config), "```", "",
              "## rocprofv3 --stats (all kernels of the run)", "", "| kernel | calls | avg us | % of GPU time |",
              "|---|---|---|---|"]
     for r in _counter_rows(os.path.join(prof_dir, stats)):
@@ -594,6 +607,7 @@ def extra_configs(args, torch, efa, synth, routing, ev, flush, stream, dedup_fit
                                                  for k in ("n", "slot_eager_us", "slot_graph_us", "dedup_eager_us",
                                                            "dedup_graph_us")} for n in range(1, 9)]}}
 
+    progress("qwen3 x48 done")
     # ---- 32-node draft tree on one Qwen3-shaped layer ----
     tl = layers[0]
     trecs = []
@@ -619,6 +633,7 @@ def extra_configs(args, torch, efa, synth, routing, ev, flush, stream, dedup_fit
     del layers, tl
     torch.cuda.empty_cache()
 
+    progress("tree done")
     # ---- Mixtral-shaped ----
     spec = synth.CONFIGS["mixtral"]
     ml = load_layout(efa.Layer(*device_layer_weights(spec, args.seed, 0), m=spec.m))
@@ -698,6 +713,7 @@ def main():
     host_w = synth.layer_weights(spec, args.seed)
     # weights in the tiled layout (moe_pack_tiled), done once at weight-load time
     layer = load_layout(efa.Layer(*(to_torch(a) for a in host_w), m=spec.m))
+    progress("%s layer on the device (%.1f s)" % (args.config, time.perf_counter() - t_setup))
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     nsteps_total = args.warmup + args.steps
@@ -782,11 +798,13 @@ def main():
     for s in range(args.warmup):
         run_step(s, False)
     torch.cuda.synchronize()
+    progress("%d warm-up steps done" % args.warmup)
     t_wall = time.perf_counter()
     for s in range(args.warmup, nsteps_total):
         run_step(s, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
+    progress("%d timed steps done (%.3f s)" % (args.steps, wall))
 
     # the shared experts' pass (read once per pass whatever the routing): D(n) of the step model
     shared_us = []
@@ -861,15 +879,19 @@ def main():
                                  "algorithmic_bytes_per_launch": round(dd_bytes / n_launch, 1)}}
 
     cpu = cpu_baseline(spec, host_w, host_passes, args.cpu_budget)
+    progress("cpu baseline done")
     extras = {}
     if not args.no_extras and args.config == "dsv2lite":
         ws9 = layer.workspace(9)
         extras["router"] = router_section(args, efa, synth, spec, passes, kinds, nvals, flush, ev, stream)
+        progress("router done")
         extras["dispatch"] = dispatch_section(args, efa, layer, ws, ys, passes, kinds, nvals, per_kind, flush, ev,
                                               stream)
+        progress("dispatch done")
         extras["chosen_ids"] = chosen_id_section(
             args, efa, routing, spec, layer, ws9, ys, flush, ev, stream, recs, per_kind,
             lambda n: to_torch(synth.pass_x(spec, args.seed, 0, 77000 + n, n)))
+        progress("chosen-id fits done")
         del ws9
     if spec.n_shared:
         extras["shared_experts"] = {"workload": "%d always-on shared experts, weight 1, every token: one "
