@@ -54,7 +54,6 @@
 
 namespace moe_k {
 
-
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
@@ -277,15 +276,14 @@ struct Smem {
     int32_t ids[MOE_MAX_SLOTS];
     int32_t grp[MOE_MAX_SLOTS];    // slots of this workgroup's unit, increasing
     uint32_t pres[MOE_MAX_EXPERTS / 32];
-    int32_t meta[4];               // [3]: id status flag
-    int32_t fin;                   // this work group finalises a split gate/up tile
+    int32_t id_status;             // set for ids out of range or repeated within a token
 };
 
 // Stable grouping of the pass's slots by expert, in LDS, for distinct expert
 // number `u` (ids in increasing order): returns e (or -1 when u >= U), g and U, and
 // with `group` writes the unit's slots, increasing, to sm.grp[0..g).  Every wave
 // computes the presence scan and the ranks itself (and writes all of sm.grp), so
-// no barrier is needed after it.  With want_status, sm.meta[3] is set for ids out
+// no barrier is needed after it.  With want_status, sm.id_status is set for ids out
 // of range or repeated within a token (read after the call by thread 0).
 template <int NB>
 __device__ void group_prologue(const Args& a, Smem<NB>& sm, int u, bool want_status, bool group, int& e_out,
@@ -295,7 +293,7 @@ __device__ void group_prologue(const Args& a, Smem<NB>& sm, int u, bool want_sta
     const int nwords = (a.N + 31) >> 5;
     __syncthreads();  // the previous unit's reads of sm are done
     if (tid < nwords) sm.pres[tid] = 0u;
-    if (tid == 0) sm.meta[3] = 0;
+    if (tid == 0) sm.id_status = 0;
     const int id = tid < nm ? a.ids[tid] : -1;
     const bool valid = tid < nm && id >= 0 && id < a.N;
     if (tid < nm) sm.ids[tid] = valid ? id : -1;
@@ -307,7 +305,7 @@ __device__ void group_prologue(const Args& a, Smem<NB>& sm, int u, bool want_sta
             const int t = tid / a.m, j = tid - t * a.m;
             for (int jj = 0; jj < j; ++jj) bad |= (sm.ids[t * a.m + jj] == id);
         }
-        if (bad) atomicOr(&sm.meta[3], 1);
+        if (bad) atomicOr(&sm.id_status, 1);
     }
     __syncthreads();
     // prefix popcount over the presence words (<= 32 words, lanes 0..31)
@@ -610,7 +608,7 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) 
             group_prologue<NT * RB>(a, sm, MODE == kDedup && !sh ? u : 0, status, MODE == kDedup && !sh, e, g, U);
             if (status && tid == 0) {
                 a.info[0] = U;
-                a.info[1] = sm.meta[3] ? MOE_E_IDS : MOE_OK;
+                a.info[1] = sm.id_status ? MOE_E_IDS : MOE_OK;
                 a.info[2] = MOE_OK;  // a bounded wait that expires later overwrites this
             }
         }
