@@ -152,7 +152,7 @@ def traffic_from(fetch_csv, write_csv, config, kernel="slot"):
     return out, per_launch
 
 
-def write_traffic_summary(fetch_csv, write_csv, config, pass_json):
+def write_traffic_summary(fetch_csv, write_csv, config, pass_json, out_dir=None):
     info = [json.loads(l) for l in open(pass_json) if l.startswith('{"pmc_pass"')][-1]
     out, per_launch = traffic_from(fetch_csv, write_csv, config)
     slot_pass = [p for p in info["pmc_pass"] if p.get("kernel", "slot") == "slot"]
@@ -198,9 +198,10 @@ def write_traffic_summary(fetch_csv, write_csv, config, pass_json):
         rec["dedup_bytes_per_launch"] = round(dper, 1)
         rec["dedup_algorithmic_bytes_per_launch"] = round(dalg, 1)
     lines += ["", "traffic-json: " + json.dumps(rec)]
-    path = os.path.join(ROOT, "profiles", "traffic_k_expert_perslot_%s.md" % config)
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), "traffic_k_expert_perslot_%s.md" % config)
     open(path, "w").write("\n".join(lines) + "\n")
     print(path)
+    return path
 
 
 def read_traffic(config):
