@@ -211,6 +211,7 @@ def _prep(layer, x, ids, w, y, ws, kind):
     _check_dev("y", y, torch.float32, (n, layer.d))
     if ws is None:
         ws = layer.workspace(n, kind)
+    _check_dev("ws", ws, torch.uint8)  # its size in bytes is ws.numel()
     return n, y, ws
 
 

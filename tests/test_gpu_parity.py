@@ -213,6 +213,10 @@ def test_accumulate_and_determinism(layout):
     efa.expert_perslot(dl.dev, xd, ids, w, y=y, ws=dl.dev.workspace(6), accumulate=True)
     torch.cuda.synchronize()
     assert torch.equal(y.cpu(), (y0 + torch.from_numpy(a[0]).cuda()).cpu())
+    say("workspace type")  # sizes are counted in bytes: a workspace is uint8 (nothing launches)
+    wsf = torch.zeros(dl.dev.workspace(6).numel() // 4 + 1, dtype=torch.float32, device="cuda")
+    with pytest.raises(TypeError):
+        efa.expert_dedup(dl.dev, xd, ids, w, ws=wsf)
 
 
 # ------------------------------ full-size layers ------------------------------
