@@ -88,22 +88,48 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(spec, host_w, passes, budget_s):
-    """The oracle, as it stands, on host cores over a bounded sample of passes."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(spec, host_w, passes, budget_s, max_threads=16):
+    """The oracle, as it stands, on host cores over a bounded sample of passes: once on
+    one thread, then the same passes spread over the process's cores (one pass per
+    thread at a time; the C call releases the GIL), whose results must be bitwise
+    equal to the single-thread ones."""
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     t0 = time.perf_counter()
     nbytes = 0
-    done = 0
+    ys = []
     for (x_h, ids, w) in passes:
-        oracle.moe_ffn(*host_w, x_h, ids, w, spec.dtype)
+        ys.append(oracle.moe_ffn(*host_w, x_h, ids, w, spec.dtype))
         nbytes += ids.size * spec.expert_bytes
-        done += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
+    done = len(ys)
+    cores = max(1, min(len(os.sched_getaffinity(0)), max_threads))
+    t1 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as pool:
+        ya = list(pool.map(lambda p: oracle.moe_ffn(*host_w, p[0], p[1], p[2], spec.dtype), passes[:done]))
+    dt_all = time.perf_counter() - t1
+    same = all(np.array_equal(a, b) for a, b in zip(ys, ya))
+    if not same:
+        raise RuntimeError("oracle results differ between one thread and %d threads" % cores)
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "%d passes (n=1..8 windows of the same traces), %.1f s, requested per-slot weight bytes / "
-                      "wall time, single-threaded C oracle (double accumulate)" % (done, dt)}
+                      "wall time, single-threaded C oracle (double accumulate)" % (done, dt),
+            "all_cores": {"value": round(nbytes / dt_all / 1e9, 4), "unit": "GB/s", "cores": cores,
+                          "seconds": round(dt_all, 2), "bitwise_equal_to_one_thread": same,
+                          "how": "the same passes, one per thread at a time"},
+            "cpu": _cpu_model()}
 
 
 PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc {counter} -d $R/gpurun_out/pmc_{tag} "

@@ -56,3 +56,24 @@ def test_traffic_summary_records_per_launch_figures(tmp_path):
     assert rec["algorithmic_bytes_per_launch"] == 4_000_000
     assert rec["dedup_bytes_per_launch"] == (500 * 2 + 2) * 1024
     assert rec["dedup_algorithmic_bytes_per_launch"] == 1_000_000
+
+
+def test_cpu_baseline_one_thread_and_all_cores():
+    """The oracle timing: one thread, then the same passes on a thread pool; the record
+    carries both rates, the thread count and the CPU model, and the pooled results are
+    bitwise those of one thread (a mismatch raises)."""
+    import synth
+    from synth import routing
+    spec = synth.layer_spec("tiny", N=8, m=2, d=64, d_ff=128, dtype="bf16")
+    W = synth.layer_weights(spec, 5)
+    passes = []
+    for p, n in enumerate((1, 3, 5, 8)):
+        tr = routing.uniform_trace(8, 2, n, routing.rng_for(5, 0, "uniform", p))
+        passes.append((synth.pass_x(spec, 5, 0, p, n), tr.ids, tr.w))
+    rec = bench.cpu_baseline(spec, W[:3], passes, 60.0, max_threads=4)
+    assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["value"] > 0
+    assert rec["sample"].startswith("4 passes")
+    ac = rec["all_cores"]
+    assert ac["bitwise_equal_to_one_thread"] is True
+    assert 1 <= ac["cores"] <= 4 and ac["value"] > 0
+    assert isinstance(rec["cpu"], str) and rec["cpu"]
