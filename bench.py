@@ -470,7 +470,11 @@ def per_n_rows(recs, nvals):
                          r=round(gd / gs, 4), u=round(bd / bs, 4),
                          us_slot=round(ts / len(R) * 1e6, 2), us_dedup=round(td / len(R) * 1e6, 2),
                          bytes_slot=bs / len(R), bytes_dedup=bd / len(R),
-                         mean_U=round(sum(r["U"] for r in R) / len(R), 2)))
+                         mean_U=round(sum(r["U"] for r in R) / len(R), 2),
+                         **{"%s_us_%s" % (stat, k): v for k in ("slot", "dedup")
+                            for stat, v in zip(("median", "q1", "q3"),
+                                               np.round(np.percentile([r["t_%s_ms" % k] * 1e3 for r in R],
+                                                                      [50, 25, 75]), 2).tolist())}))
     return rows
 
 
@@ -944,6 +948,8 @@ def main():
                args.config, nvals[-1], "+".join(k for k, _ in kinds)),
                "N": spec.N, "m": spec.m, "d_model": spec.d, "d_ff": spec.d_ff, "weight_layout": WEIGHT_LAYOUT,
                "passes_per_step": len(kinds) * len(nvals) * 2,
+               "launches_per_pass": {"slot": efa.kernels_per_call(efa.MOE_KIND_SLOT),
+                                     "dedup": efa.kernels_per_call(efa.MOE_KIND_DEDUP)},
                "scrub_bytes": 0 if args.no_scrub else SCRUB_BYTES},
            "roofline": roofline, "cpu_baseline": cpu, "results": per_kind, "extras": extras,
            "wall_s_timed": round(wall, 3), "setup_s": round(setup_s, 1), "source_hash": source_hash()}
