@@ -98,6 +98,9 @@ def _cpu_model():
     return "unknown"
 
 
+HOST_WINDOWS = 6  # windows per (routing, n) offered to the oracle's timed sample
+
+
 def cpu_baseline(spec, host_w, passes, budget_s, max_threads=16):
     """The oracle, as it stands, on host cores over a bounded sample of passes: once on
     one thread, then the same passes spread over the process's cores (one pass per
@@ -124,7 +127,7 @@ def cpu_baseline(spec, host_w, passes, budget_s, max_threads=16):
     if not same:
         raise RuntimeError("oracle results differ between one thread and %d threads" % cores)
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d passes (n=1..8 windows of the same traces), %.1f s, requested per-slot weight bytes / "
+            "sample": "%d passes (windows of the same traces, every n and routing in turn), %.1f s, requested per-slot weight bytes / "
                       "wall time, single-threaded C oracle (double accumulate)" % (done, dt),
             "all_cores": {"value": round(nbytes / dt_all / 1e9, 4), "unit": "GB/s", "cores": cores,
                           "seconds": round(dt_all, 2), "bitwise_equal_to_one_thread": same,
@@ -763,8 +766,10 @@ def main():
                 dev = (to_torch(x_h), torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda())
                 passes[(kind, n, s)] = dict(x=dev[0], ids=dev[1], w=dev[2], ids_h=ids,
                                             U=len(set(ids.reshape(-1).tolist())))
-                if s == 0:
-                    host_passes.append((x_h, ids, w))
+                if s < HOST_WINDOWS:
+                    host_passes.append(((s, ki, n), (x_h, ids, w)))
+    # the oracle's sample: window by window, each over both routings and every n
+    host_passes = [p for _, p in sorted(host_passes, key=lambda e: e[0])]
     ws = layer.workspace(nvals[-1])  # zero-filled once; serves every n
     ys = {n: torch.empty(n, spec.d, dtype=torch.float32, device="cuda") for n in nvals}
     scrub = torch.ones(SCRUB_BYTES // 4, dtype=torch.float32, device="cuda")
