@@ -77,3 +77,16 @@ def test_cpu_baseline_one_thread_and_all_cores():
     assert ac["bitwise_equal_to_one_thread"] is True
     assert 1 <= ac["cores"] <= 4 and ac["value"] > 0
     assert isinstance(rec["cpu"], str) and rec["cpu"]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """One GPU is measured: --gpus above 1 exits with status 2 and says why, before any
+    device work."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    p = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=60)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr and p.stdout == ""
