@@ -318,3 +318,20 @@ def test_c_program_uses_the_abi(tmp_path):
     assert out["failures"] == "0"
     d = _desc(N=64, m=6, d_model=2048, d_ff=1408, dtype=_abi.MOE_BF16)
     assert int(out["workspace_slot_n8"]) == _abi.lib().moe_workspace_bytes(ctypes.byref(d), 8, 0)
+
+
+def test_missing_library_fails_loudly():
+    """Without the built library every op raises at once: there is no other path."""
+    import subprocess
+    import sys
+    code = ("import expert_ffn_amd as efa\n"
+            "from expert_ffn_amd import _abi\n"
+            "_abi.SO_PATH = _abi.SO_PATH + '.absent'\n"
+            "try:\n"
+            "    efa.kernels_per_call(efa.MOE_KIND_SLOT)\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    p = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, cwd=root)
+    assert p.returncode == 0, p.stderr
+    assert p.stdout.startswith("raised:") and "not built" in p.stdout
