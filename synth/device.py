@@ -23,7 +23,8 @@ def device_layer_weights(spec, seed, layer=0, device="cuda"):
     makes the host generator too slow (58 GB for 48 Qwen3-shaped layers).  Same
     law as ``layers.layer_weights`` (sigma * N(0, 1), rounded to the layer dtype),
     drawn from torch's seeded device generator, one stream per (seed, layer,
-    tensor); not the host generator's values, so parity tests do not use them."""
+    tensor), one draw per tensor; not the host generator's values, so parity
+    tests do not use them."""
     from . import lib
     from .layers import TAG_DOWN, TAG_GATE, TAG_UP
     dt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
@@ -32,8 +33,6 @@ def device_layer_weights(spec, seed, layer=0, device="cuda"):
                        (TAG_DOWN, (spec.N, spec.d, spec.d_ff))):
         g = torch.Generator(device=device)
         g.manual_seed(lib.key_of(seed, layer, tag, 0xD) & ((1 << 63) - 1))
-        t = torch.empty(shape, dtype=dt, device=device)
-        for e in range(spec.N):  # per expert, so the fp32 temporary stays small
-            t[e].copy_(torch.randn(shape[1:], generator=g, device=device, dtype=torch.float32).mul_(spec.sigma))
+        t = torch.randn(shape, generator=g, device=device, dtype=torch.float32).mul_(spec.sigma).to(dt)
         out.append(t)
     return tuple(out)

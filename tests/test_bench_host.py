@@ -1,7 +1,13 @@
-"""The bench's counter bookkeeping on the host (no GPU): FETCH_SIZE / WRITE_SIZE rows of
-a counter run are calibrated by the run's device copy, split by kernel (per-slot,
-deduplicating) and averaged per launch; the summary file carries the per-launch
-figures and the kernel source hash."""
+"""The bench's host-side bookkeeping (no GPU).
+
+* Counters: FETCH_SIZE / WRITE_SIZE rows of a counter run are calibrated by the run's
+  device copy, split by kernel (per-slot, deduplicating) and averaged per launch; the
+  summary file carries the per-launch figures and the kernel source hash.
+* Aggregation (Lan Section 2, Table 1 caption): beta, r and u from bytes and times
+  summed over windows; the crossover as the smallest n from which the saving stays
+  positive; both against records computed by hand.
+* The final line: compact (a few KB), with the fields the metric needs.
+"""
 import csv
 import json
 
@@ -34,34 +40,34 @@ def _runs(tmp_path):
 
 def test_traffic_is_calibrated_and_split_by_kernel(tmp_path):
     fp, wp = _runs(tmp_path)
-    out, per_launch = bench.traffic_from(fp, wp, "dsv2lite")
+    out, per_launch = bench.traffic_from(fp, wp)
     assert abs(out["fetch"]["factor"] - 2.0) < 1e-12 and abs(out["write"]["factor"] - 1.0) < 1e-12
     assert out["fetch"]["bytes"] == [1000 * 1024 * 2.0, 3000 * 1024 * 2.0]
     assert per_launch == ((1000 + 3000) * 2 + (4 + 8)) * 1024 / 2
-    dout, dper = bench.traffic_from(fp, wp, "dsv2lite", kernel="dedup")
+    dout, dper = bench.traffic_from(fp, wp, kernel="dedup")
     assert dout["fetch"]["bytes"] == [500 * 1024 * 2.0] and dper == (500 * 2 + 2) * 1024
 
 
 def test_traffic_summary_records_per_launch_figures(tmp_path):
     fp, wp = _runs(tmp_path)
-    passes = [dict(kernel="slot", kind="uniform", n=1, U=6, bytes=2_000_000),
-              dict(kernel="slot", kind="uniform", n=2, U=11, bytes=6_000_000),
-              dict(kernel="dedup", kind="uniform", n=2, U=11, bytes=1_000_000)]
+    passes = [dict(kernel="slot", n=1, layer=0, U=8, bytes=2_000_000),
+              dict(kernel="slot", n=2, layer=0, U=15, bytes=6_000_000),
+              dict(kernel="dedup", n=2, layer=0, U=15, bytes=1_000_000)]
     log = tmp_path / "pmc.log"
     log.write_text("noise\n" + json.dumps({"pmc_pass": passes, "source_hash": "abc"}) + "\n")
-    path = bench.write_traffic_summary(fp, wp, "dsv2lite", str(log), out_dir=str(tmp_path))
+    path = bench.write_traffic_summary(fp, wp, str(log), out_dir=str(tmp_path))
     rec = json.loads([l for l in open(path) if l.startswith("traffic-json: ")][0][len("traffic-json: "):])
-    assert rec["source_hash"] == "abc" and rec["launches"] == 2
-    assert rec["bytes_per_launch"] == ((1000 + 3000) * 2 + (4 + 8)) * 1024 / 2
-    assert rec["algorithmic_bytes_per_launch"] == 4_000_000
+    assert rec["source_hash"] == "abc" and rec["slot_launches"] == 2 and rec["dedup_launches"] == 1
+    assert rec["slot_bytes_per_launch"] == ((1000 + 3000) * 2 + (4 + 8)) * 1024 / 2
+    assert rec["slot_algorithmic_bytes_per_launch"] == 4_000_000
     assert rec["dedup_bytes_per_launch"] == (500 * 2 + 2) * 1024
     assert rec["dedup_algorithmic_bytes_per_launch"] == 1_000_000
 
 
 def test_cpu_baseline_one_thread_and_all_cores():
     """The oracle timing: one thread, then the same passes on a thread pool; the record
-    carries both rates, the thread count and the CPU model, and the pooled results are
-    bitwise those of one thread (a mismatch raises)."""
+    carries both rates, the thread count, nproc and the CPU model, and the pooled results
+    are bitwise those of one thread (a mismatch raises)."""
     import synth
     from synth import routing
     spec = synth.layer_spec("tiny", N=8, m=2, d=64, d_ff=128, dtype="bf16")
@@ -69,14 +75,83 @@ def test_cpu_baseline_one_thread_and_all_cores():
     passes = []
     for p, n in enumerate((1, 3, 5, 8)):
         tr = routing.uniform_trace(8, 2, n, routing.rng_for(5, 0, "uniform", p))
-        passes.append((synth.pass_x(spec, 5, 0, p, n), tr.ids, tr.w))
-    rec = bench.cpu_baseline(spec, W[:3], passes, 60.0, max_threads=4)
-    assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["value"] > 0
+        passes.append((W, synth.pass_x(spec, 5, 0, p, n), tr.ids, tr.w, "bf16", n * 2 * spec.expert_bytes))
+    rec = bench.cpu_baseline(passes, 60.0, max_threads=4)
+    assert rec["kind"] == "oracle" and rec["value"] > 0 and rec["unit"] == "GB/s"
     assert rec["sample"].startswith("4 passes")
-    ac = rec["all_cores"]
-    assert ac["bitwise_equal_to_one_thread"] is True
-    assert 1 <= ac["cores"] <= 4 and ac["value"] > 0
-    assert isinstance(rec["cpu"], str) and rec["cpu"]
+    assert rec["bitwise_equal_to_one_thread"] is True
+    assert 1 <= rec["cores"] <= 4 and rec["one_thread"]["value"] > 0
+    assert rec["nproc"] >= 1 and isinstance(rec["cpu"], str) and rec["cpu"]
+
+
+def _rec(n, U, ts_us, td_us, m=8, w=100_000):
+    return dict(n=n, U=U, bytes_slot=n * m * w, bytes_dedup=U * w, t_slot_ms=ts_us / 1e3, t_dedup_ms=td_us / 1e3)
+
+
+def test_per_n_rows_sums_bytes_and_times():
+    """beta_p = summed bytes / summed times over the windows of one n; r = beta_dedup /
+    beta_slot; u = E_dedup / E_slot; quartiles over the windows' times (by hand)."""
+    recs = [_rec(2, 10, 2.0, 1.0), _rec(2, 14, 4.0, 3.0), _rec(2, 12, 3.0, 5.0), _rec(1, 8, 1.0, 1.25)]
+    rows = bench.per_n_rows(recs, [1, 2])
+    r1, r2 = rows
+    # n = 1: 800 kB in 1 us per-slot (800 GB/s), 800 kB in 1.25 us dedup (640 GB/s)
+    assert r1["windows"] == 1 and r1["gbps_slot"] == 800.0 and r1["gbps_dedup"] == 640.0
+    assert r1["r"] == 0.8 and r1["u"] == 1.0 and r1["frac_slot"] == 0.1
+    # n = 2: per-slot 3 x 1.6 MB in 9 us, dedup (1.0 + 1.4 + 1.2) MB in 9 us
+    assert r2["windows"] == 3 and r2["bytes_slot"] == 1_600_000 and r2["bytes_dedup"] == 1_200_000
+    assert r2["gbps_slot"] == round(4.8e6 / 9e-6 / 1e9, 1) and r2["gbps_dedup"] == 400.0
+    assert r2["r"] == 0.75 and r2["u"] == 0.75
+    assert r2["us_slot"] == 3.0 and r2["us_dedup"] == 3.0 and r2["mean_U"] == 12.0
+    assert (r2["q1_us_slot"], r2["median_us_slot"], r2["q3_us_slot"]) == (2.5, 3.0, 3.5)
+    assert (r2["q1_us_dedup"], r2["median_us_dedup"], r2["q3_us_dedup"]) == (2.0, 3.0, 4.0)
+
+
+def test_crossover_is_where_the_saving_stays_positive():
+    def rows(S):  # S[n] = t_slot - t_dedup for n = 1..len(S)
+        return [dict(n=i + 1, us_slot=10.0 + s, us_dedup=10.0) for i, s in enumerate(S)]
+    assert bench.crossover_of(rows([0, -1, 2, 3, 1])) == 3
+    assert bench.crossover_of(rows([0, 1, 2, 3])) == 2
+    assert bench.crossover_of(rows([5, 1, -2, 3, 0])) == 0     # S(5) = 0 is not a saving
+    assert bench.crossover_of(rows([5, 1, 2, -1, 3])) == 5
+    assert bench.crossover_of(rows([-1])) == 0                  # n = 1 alone has no crossover
+
+
+def test_headline_line_is_compact_and_complete():
+    """The final stdout line: at most 4 KB, with value = summed bytes / summed times over
+    both kernels, ms_per_step = summed times / steps, the roofline of the kernel with the
+    most time (its per-n and n = 1 fractions for both kernels) and the oracle baseline."""
+    import argparse
+    recs = [_rec(n, 8 + 3 * (n - 1), 20.0 * n, 12.0 * n + 10, m=8, w=9_437_184 * 48) for n in range(1, 9)
+            for _ in range(20)]
+    rows = bench.per_n_rows(recs, list(range(1, 9)))
+    head = {"recs": recs, "rows": rows, "crossover": bench.crossover_of(rows),
+            "step_model": {"kstar_slot": [0] * 22, "kstar_dedup": [1] * 22, "crossover_model": 2}}
+    pk = {"uniform": {"per_n": rows, "crossover": 5}, "correlated": {"per_n": rows, "crossover": 2}}
+    others = {("dsv2lite_" + k): v for k, v in bench.other_summary(pk).items()}
+    others.update({("mixtral_" + k): v for k, v in bench.other_summary(pk).items()})
+    others["tree"] = {"r": 0.6, "u": 0.33, "U": 85.2, "us_slot": 330.0, "us_dedup": 180.0, "frac": [0.9, 0.6]}
+    cpu = {"value": 55.1, "unit": "GB/s", "cores": 16, "kind": "oracle", "sample": "x" * 300,
+           "one_thread": {"value": 4.3, "seconds": 12.0}, "nproc": 256, "affinity": 16, "cpu": "some cpu model name",
+           "seconds": 1.0, "bitwise_equal_to_one_thread": True}
+    args = argparse.Namespace(steps=20, warmup=5, reps=3, no_scrub=False)
+    line = bench.headline_line(args, head, others, cpu, list(range(1, 9)), 48, "gpurun_out/bench_full.json")
+    text = json.dumps(line, separators=(",", ":"))
+    assert len(text) <= 4096, len(text)
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+              "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert k in line, k
+    tb = sum(r["bytes_slot"] + r["bytes_dedup"] for r in recs)
+    ts = sum(r["t_slot_ms"] + r["t_dedup_ms"] for r in recs) / 1e3
+    assert line["value"] == round(tb / ts / 1e9, 1) and line["ms_per_step"] == round(ts * 1e3 / 20, 4)
+    rf = line["roofline"]
+    assert rf["bound"] == "hbm" and rf["peak"] == 8000.0 and rf["unit"] == "GB/s"
+    assert "per-slot" in rf["kernel"]  # the per-slot kernel has the more time here
+    sb = sum(r["bytes_slot"] for r in recs) / (len(recs) * 48)
+    st = sum(r["t_slot_ms"] for r in recs) / 1e3 / (len(recs) * 48)
+    assert rf["achieved"] == round(sb / st / 1e9, 1) and rf["frac"] == round(sb / st / 1e9 / 8000.0, 4)
+    assert rf["frac_n1_slot"] == rows[0]["frac_slot"] and rf["frac_n1_dedup"] == rows[0]["frac_dedup"]
+    assert len(rf["frac_per_n_slot"]) == 8 and len(line["per_n"]["r"]) == 8
+    assert line["cpu_baseline"]["kind"] == "oracle" and line["config"]["windows_per_n"] == 20
 
 
 def test_bench_refuses_more_than_one_gpu():
