@@ -52,6 +52,7 @@ COPY_BYTES = 1 << 28
 A_GRID = [i / 21.0 for i in range(22)]  # acceptance values of the best-draft-length staircase
 HEADLINE = "qwen3x48"
 WORKLOADS = ("qwen3x48", "tree", "dsv2lite", "mixtral")
+PMC_TREES = 8          # seeded trees in a counter run
 ORACLE_LAYERS = 2      # headline layers whose plain weights stay resident for the oracle's sample
 HOST_WINDOWS = 6       # windows per n offered to the oracle's timed sample
 MAX_POOL = 16          # host threads for the oracle: one GPU's share of the host's cores
@@ -282,65 +283,164 @@ def traffic_from(fetch_csv, write_csv, kernel="slot"):
     return out, per_launch
 
 
+def _workloads_of(order):
+    seen = []
+    for p in order:
+        if p["workload"] not in seen:
+            seen.append(p["workload"])
+    return seen
+
+
 def write_traffic_summary(fetch_csv, write_csv, pass_json, out_dir=None):
-    """profiles/traffic_k_expert_qwen3x48.md from the two counter runs: per (kernel,
-    n) the launches' fetched and written bytes against the algorithmic bytes, and
-    per kernel the bytes per launch (the `traffic` of the roofline)."""
+    """profiles/traffic_k_expert.md from the two counter runs of `--pmc-pass`: per
+    workload, kernel and n the launches' fetched and written bytes against the
+    algorithmic bytes (n m w per-slot, U w deduplicating), and per workload and kernel
+    the counted bytes per launch (the headline's are the roofline's `traffic`)."""
     info = [json.loads(l) for l in open(pass_json) if l.startswith('{"pmc_pass"')][-1]
-    lines = ["# HBM traffic of k_expert, qwen3-shaped layer x48 per pass, zipf routing, n = 1..8",
+    lines = ["# HBM traffic of k_expert per launch: every workload of the bench, both kernels",
              "", "Commands (one GPU; FETCH_SIZE and WRITE_SIZE in separate runs), then on any host:", "", "```",
              PMC_CMD.format(counter="FETCH_SIZE", tag="fetch"), PMC_CMD.format(counter="WRITE_SIZE", tag="write"),
              "python3 bench.py --traffic-from gpurun_out/pmc_fetch/run_counter_collection.csv "
-             "gpurun_out/pmc_write/run_counter_collection.csv gpurun_out/pmc_fetch.log", "```", ""]
-    rec = {"config": HEADLINE, "source_hash": info["source_hash"]}
-    for kernel, label in (("slot", "per-slot"), ("dedup", "deduplicating")):
+             "gpurun_out/pmc_write/run_counter_collection.csv gpurun_out/pmc_fetch.log", "```", "",
+             "One window per (routing, n) (the headline: one window per n, 48 layers; the tree: %d seeded trees), each "
+             "launch after the 1 GiB read flush. Algorithmic bytes: n m w per-slot, U w deduplicating (U distinct "
+             "experts of the layer)." % PMC_TREES, ""]
+    rec = {"source_hash": info["source_hash"], "per_launch": {}}
+    data = {}
+    for kernel in ("slot", "dedup"):
         order = [p for p in info["pmc_pass"] if p["kernel"] == kernel]
-        out, per_launch = traffic_from(fetch_csv, write_csv, kernel=kernel)
+        out, _ = traffic_from(fetch_csv, write_csv, kernel=kernel)
         assert len(order) == len(out["fetch"]["bytes"]), (kernel, len(order), len(out["fetch"]["bytes"]))
-        if kernel == "slot":
-            lines += ["Calibration: the run's device copy of %d bytes reads %.1f KiB FETCH_SIZE and %.1f KiB "
-                      "WRITE_SIZE, so the counters are scaled by %.4f and %.4f." % (
-                          COPY_BYTES, out["fetch"]["copy_kib"], out["write"]["copy_kib"], out["fetch"]["factor"],
-                          out["write"]["factor"]), ""]
-        lines += ["## %s kernel (algorithmic bytes: %s per layer)" % (
-            label, "n m w" if kernel == "slot" else "U w, U the layer's distinct experts"), "",
-            "| n | launches | mean U | algorithmic MB per launch | fetched MB | written MB | fetched / algorithmic |",
-            "|---|---|---|---|---|---|---|"]
-        for n in sorted(set(p["n"] for p in order)):
-            idx = [i for i, p in enumerate(order) if p["n"] == n]
-            alg = sum(order[i]["bytes"] for i in idx)
-            fb = sum(out["fetch"]["bytes"][i] for i in idx)
-            wb = sum(out["write"]["bytes"][i] for i in idx)
-            lines.append("| %d | %d | %.2f | %.2f | %.2f | %.3f | %.3f |" % (
-                n, len(idx), sum(order[i]["U"] for i in idx) / len(idx), alg / len(idx) / 1e6, fb / len(idx) / 1e6,
-                wb / len(idx) / 1e6, fb / alg))
-        alg_pl = sum(p["bytes"] for p in order) / len(order)
-        lines += ["", "Per launch (average over the %d launches): %.2f MB counted (fetched + written), %.2f MB "
-                  "algorithmic." % (len(order), per_launch / 1e6, alg_pl / 1e6), ""]
-        rec["%s_bytes_per_launch" % kernel] = round(per_launch, 1)
-        rec["%s_algorithmic_bytes_per_launch" % kernel] = round(alg_pl, 1)
-        rec["%s_launches" % kernel] = len(order)
+        data[kernel] = (order, out)
+    out = data["slot"][1]
+    lines += ["Calibration: the run's device copy of %d bytes reads %.1f KiB FETCH_SIZE and %.1f KiB WRITE_SIZE, so "
+              "the counters are scaled by %.4f and %.4f." % (COPY_BYTES, out["fetch"]["copy_kib"],
+                                                             out["write"]["copy_kib"], out["fetch"]["factor"],
+                                                             out["write"]["factor"]), ""]
+    for wl in _workloads_of(info["pmc_pass"]):
+        lines += ["## %s" % wl, "",
+                  "| n | launches | mean U | per-slot alg. MB | fetched MB | fetched / alg. | written MB | "
+                  "dedup alg. MB | fetched MB | fetched / alg. | written MB |",
+                  "|---|---|---|---|---|---|---|---|---|---|---|"]
+        rec["per_launch"][wl] = {}
+        cells = {}
+        for kernel in ("slot", "dedup"):
+            order, out = data[kernel]
+            idx = [i for i, p in enumerate(order) if p["workload"] == wl]
+            if not idx:
+                continue
+            for n in sorted(set(order[i]["n"] for i in idx)):
+                ii = [i for i in idx if order[i]["n"] == n]
+                alg = sum(order[i]["bytes"] for i in ii) / len(ii)
+                fb = sum(out["fetch"]["bytes"][i] for i in ii) / len(ii)
+                wb = sum(out["write"]["bytes"][i] for i in ii) / len(ii)
+                cells.setdefault(n, {"launches": len(ii), "U": sum(order[i]["U"] for i in ii) / len(ii)})
+                cells[n][kernel] = (alg, fb, wb)
+            cnt = sum(out["fetch"]["bytes"][i] + out["write"]["bytes"][i] for i in idx) / len(idx)
+            rec["per_launch"][wl][kernel] = {"bytes": round(cnt, 1), "launches": len(idx),
+                                             "algorithmic": round(sum(order[i]["bytes"] for i in idx) / len(idx), 1),
+                                             "fetched_over_algorithmic": round(
+                                                 sum(out["fetch"]["bytes"][i] for i in idx) /
+                                                 sum(order[i]["bytes"] for i in idx), 4)}
+        for n in sorted(cells):
+            c = cells[n]
+            row = ["%d" % n, "%d" % c["launches"], "%.2f" % c["U"]]
+            for kernel in ("slot", "dedup"):
+                if kernel in c:
+                    a, f, w = c[kernel]
+                    row += ["%.1f" % (a / 1e6), "%.1f" % (f / 1e6), "%.3f" % (f / a), "%.2f" % (w / 1e6)]
+                else:
+                    row += ["-"] * 4
+            lines.append("| " + " | ".join(row) + " |")
+        lines += [""] + ["Per launch, %s kernel: %.2f MB counted (fetched + written) for %.2f MB algorithmic." % (
+            kernel, v["bytes"] / 1e6, v["algorithmic"] / 1e6) for kernel, v in rec["per_launch"][wl].items()] + [""]
     rec["fetch_factor"] = round(out["fetch"]["factor"], 4)
     rec["write_factor"] = round(out["write"]["factor"], 4)
     lines += ["traffic-json: " + json.dumps(rec)]
-    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), "traffic_k_expert_%s.md" % HEADLINE)
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), "traffic_k_expert.md")
     open(path, "w").write("\n".join(lines) + "\n")
     print(path)
     return path
 
 
-def read_traffic(kernel="slot"):
-    """Counted HBM bytes per launch from the committed counter summary of the headline
-    workload, if it was taken on this kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", "traffic_k_expert_%s.md" % HEADLINE)
+def read_traffic(kernel="slot", workload=HEADLINE):
+    """Counted HBM bytes per launch from the committed counter summary, if it was
+    taken on this kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic_k_expert.md")
     if not os.path.exists(path):
         return None
     for line in open(path):
         if line.startswith("traffic-json: "):
             rec = json.loads(line[len("traffic-json: "):])
             if rec.get("source_hash") == source_hash():
-                return rec.get("%s_bytes_per_launch" % kernel)
+                return rec["per_launch"].get(workload, {}).get(kernel, {}).get("bytes")
     return None
+
+
+SQ_A = ("SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_BUSY_CYCLES "
+        "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_MFMA GRBM_GUI_ACTIVE")
+SQ_B = ("SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS SQ_INSTS_VALU SQ_INST_CYCLES_VMEM_RD SQ_INSTS_SALU "
+        "SQ_CYCLES GRBM_GUI_ACTIVE")
+SQ_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc {counters} -d $R/gpurun_out/pmc_{tag} "
+          "-o run --output-format csv -- python3 $R/bench.py --pmc-pass > $R/gpurun_out/pmc_{tag}.log")
+
+
+def _per_dispatch(path, tag):
+    """{dispatch id: {counter: value, "_us": duration}} of the dispatches whose kernel
+    name contains `tag`, in dispatch order."""
+    import collections
+    d = collections.OrderedDict()
+    for r in _counter_rows(path):
+        if tag not in r["Kernel_Name"]:
+            continue
+        key = int(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        e = d.setdefault(key, {})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if "Start_Timestamp" in r and r["Start_Timestamp"]:
+            e["_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000
+    return list(d.values())
+
+
+def write_sq_summary(csv_a, csv_b, pass_json, out_dir=None):
+    """profiles/k_expert_sq_counters.md: instruction-level counters of the `--pmc-pass`
+    launches, averaged per (workload, kernel), with the share of wave cycles spent
+    waiting, the MFMA work against the dense bf16 peak and the VALU activity."""
+    info = [json.loads(l) for l in open(pass_json) if l.startswith('{"pmc_pass"')][-1]
+    lines = ["# k_expert instruction-level counters: every workload of the bench, both kernels", "",
+             "Two counter runs over the launches of the traffic summary, then on any host (R = repository root):", "",
+             "```", SQ_CMD.format(counters=SQ_A, tag="sqa"), SQ_CMD.format(counters=SQ_B, tag="sqb"),
+             "python3 bench.py --sq-summary gpurun_out/pmc_sqa/run_counter_collection.csv "
+             "gpurun_out/pmc_sqb/run_counter_collection.csv gpurun_out/pmc_sqa.log", "```", "",
+             "Averages per launch. wait share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (the share of wave cycles spent "
+             "waiting on operands); MFMA share = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flops / duration / 2.5 PFLOP/s "
+             "(dense bf16 peak); VALU per wave = SQ_INSTS_VALU / SQ_WAVES; LDS conflict share = "
+             "SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS. Source hash %s." % info["source_hash"], "",
+             "| workload | kernel | launches | µs | waves | wait share | MFMA share | VALU per wave | LDS conflict share |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    out = {}
+    for kernel, mode in (("slot", 0), ("dedup", 1)):
+        order = [p for p in info["pmc_pass"] if p["kernel"] == kernel]
+        A = _per_dispatch(csv_a, "k_expert<true, %d," % mode)
+        B = _per_dispatch(csv_b, "k_expert<true, %d," % mode)
+        assert len(A) == len(B) == len(order), (kernel, len(A), len(B), len(order))
+        for wl in _workloads_of(order):
+            idx = [i for i, p in enumerate(order) if p["workload"] == wl]
+
+            def avg(X, c):
+                return sum(X[i].get(c, 0.0) for i in idx) / len(idx)
+            us = avg(A, "_us")
+            wait = avg(A, "SQ_WAIT_INST_ANY") / max(avg(A, "SQ_WAVE_CYCLES"), 1.0)
+            mfma = avg(A, "SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512 / max(us * 1e-6, 1e-12) / 2.5e15
+            valu = avg(B, "SQ_INSTS_VALU") / max(avg(A, "SQ_WAVES"), 1.0)
+            lds = avg(B, "SQ_LDS_BANK_CONFLICT") / max(avg(B, "SQ_ACTIVE_INST_LDS"), 1.0)
+            out.setdefault(wl, {})[kernel] = dict(us=us, wait=wait, mfma=mfma)
+            lines.append("| %s | %s | %d | %.1f | %.0f | %.3f | %.4f | %.0f | %.4f |" % (
+                wl, kernel, len(idx), us, avg(A, "SQ_WAVES"), wait, mfma, valu, lds))
+    lines += ["", "sq-json: " + json.dumps({"source_hash": info["source_hash"], "per_launch": out})]
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), "k_expert_sq_counters.md")
+    open(path, "w").write("\n".join(lines) + "\n")
+    print(path)
+    return path
 
 
 def write_profile_summary(prof_dir, bench_json):
@@ -644,8 +744,8 @@ def qwen3x48(args, torch, efa, synth, routing, clock, nvals, full):
                 raise RuntimeError("expert call failed: status %d" % rc)
 
     if args.pmc_pass:
-        # Counter run: one window per n, each kernel once per pass after the flush,
-        # then a device copy of COPY_BYTES that calibrates FETCH_SIZE and WRITE_SIZE.
+        # Counter run: one window per n, each kernel once per pass after the flush;
+        # then the 32-node tree on layer 0 (a few seeded trees)
         order = []
         for kname, fn in (("slot", lib.moe_expert_perslot), ("dedup", lib.moe_expert_dedup)):
             for n in nvals:
@@ -654,16 +754,22 @@ def qwen3x48(args, torch, efa, synth, routing, clock, nvals, full):
                 run_all(fn, argsets(n, s))
                 for l in range(L):
                     Ul = int(dev[n]["U"][s, l])
-                    order.append(dict(kernel=kname, n=n, layer=l, U=Ul,
+                    order.append(dict(workload=HEADLINE, kernel=kname, n=n, layer=l, U=Ul,
                                       bytes=(n * spec.m if kname == "slot" else Ul) * w_exp))
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
+        x = xdev(torch, spec, (32,), 77)
+        y = torch.empty(32, spec.d, dtype=torch.float32, device="cuda")
+        ws32 = layers[0].workspace(32)
+        for i in range(PMC_TREES):
+            _, ttr = routing.tree_routing(spec.N, spec.m, 0.5, routing.rng_for(args.seed, 0, "tree", 100000 + i))
+            ids, w = torch.from_numpy(ttr.ids).cuda(), torch.from_numpy(ttr.w).cuda()
+            U = len(set(ttr.ids.reshape(-1).tolist()))
+            for kname, fn in (("slot", efa.expert_perslot), ("dedup", efa.expert_dedup)):
+                clock.flush()
+                fn(layers[0], x, ids, w, y=y, ws=ws32)
+                order.append(dict(workload="tree", kernel=kname, n=32, layer=0, U=U,
+                                  bytes=(32 * spec.m if kname == "slot" else U) * w_exp))
         torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"pmc_pass": order, "flush_read_bytes": SCRUB_BYTES, "copy_bytes": COPY_BYTES,
-                          "source_hash": source_hash()}))
-        return None
+        return {"pmc_order": order}
 
     recs = []
     for n in nvals:
@@ -765,6 +871,32 @@ def prepare_windows(args, torch, synth, routing, spec, kinds, nvals, host_x=True
                 passes[(kind, n, s)] = dict(x=x, ids=torch.from_numpy(ids).cuda(), w=torch.from_numpy(w).cuda(),
                                             ids_h=ids, w_h=w, U=len(set(ids.reshape(-1).tolist())))
     return passes
+
+
+def pmc_single_layer(args, torch, efa, synth, routing, clock, nvals, name):
+    """Counter run of a single-layer workload: one window per (routing, n), each
+    kernel once after the flush; returns what ran, in dispatch order."""
+    from synth.device import device_layer_weights
+    spec = synth.CONFIGS[name]
+    kinds = {"dsv2lite": [("uniform", {}), ("correlated", {"p": 0.5})],
+             "mixtral": [("uniform", {}), ("correlated", {"p": 0.6})]}[name]
+    layer = load_layout(efa.Layer(*device_layer_weights(spec, args.seed, 0), m=spec.m))
+    one = argparse.Namespace(**{**vars(args), "steps": 1, "warmup": 0})
+    passes = prepare_windows(one, torch, synth, routing, spec, kinds, nvals, host_x=False)
+    ws = layer.workspace(nvals[-1])
+    order = []
+    for kind, _ in kinds:
+        for n in nvals:
+            p = passes[(kind, n, 0)]
+            y = torch.empty(n, spec.d, dtype=torch.float32, device="cuda")
+            for kname, fn in (("slot", efa.expert_perslot), ("dedup", efa.expert_dedup)):
+                clock.flush()
+                fn(layer, p["x"], p["ids"], p["w"], y=y, ws=ws)
+                order.append(dict(workload="%s_%s" % (name, kind), kernel=kname, n=n, layer=0, U=p["U"],
+                                  bytes=(n * spec.m if kname == "slot" else p["U"]) * spec.expert_bytes))
+    torch.cuda.synchronize()
+    del layer
+    return order
 
 
 def dsv2lite(args, torch, efa, synth, routing, clock, nvals):
@@ -971,7 +1103,9 @@ def main():
                     help="for a counter run: one window per n of the headline workload, both kernels, each pass "
                          "after the 1 GiB read flush, then a 256 MiB device copy; prints what ran")
     ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "PASS_LOG"),
-                    help="write profiles/traffic_k_expert_qwen3x48.md from two counter runs (no GPU)")
+                    help="write profiles/traffic_k_expert.md from two counter runs (no GPU)")
+    ap.add_argument("--sq-summary", nargs=3, metavar=("SQA_CSV", "SQB_CSV", "PASS_LOG"),
+                    help="write profiles/k_expert_sq_counters.md from two counter runs (no GPU)")
     ap.add_argument("--profile-summary", nargs=2, metavar=("PROF_DIR", "BENCH_JSON"),
                     help="write profiles/k_expert_qwen3x48.md from a kernel-trace run (no GPU)")
     args = ap.parse_args()
@@ -980,6 +1114,9 @@ def main():
         return
     if args.profile_summary:
         write_profile_summary(*args.profile_summary)
+        return
+    if args.sq_summary:
+        write_sq_summary(*args.sq_summary)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the expert operation here runs on a single MI355X and has no "
@@ -1003,7 +1140,20 @@ def main():
     t_all = time.perf_counter()
 
     head = qwen3x48(args, torch, efa, synth, routing, clock, nvals, full=True)
-    if head is None:  # counter run
+    if args.pmc_pass:  # counter run: the other single-layer workloads, then the calibration copy
+        order = head["pmc_order"]
+        del head
+        torch.cuda.empty_cache()
+        order += pmc_single_layer(args, torch, efa, synth, routing, clock, nvals, "dsv2lite")
+        torch.cuda.empty_cache()
+        order += pmc_single_layer(args, torch, efa, synth, routing, clock, nvals, "mixtral")
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_pass": order, "flush_read_bytes": SCRUB_BYTES, "copy_bytes": COPY_BYTES,
+                          "source_hash": source_hash()}))
         return
     full = {"headline": {k: v for k, v in head.items() if k not in ("recs", "rows", "cpu_passes", "cpu_sample",
                                                                      "layer0")},

@@ -50,18 +50,21 @@ def test_traffic_is_calibrated_and_split_by_kernel(tmp_path):
 
 def test_traffic_summary_records_per_launch_figures(tmp_path):
     fp, wp = _runs(tmp_path)
-    passes = [dict(kernel="slot", n=1, layer=0, U=8, bytes=2_000_000),
-              dict(kernel="slot", n=2, layer=0, U=15, bytes=6_000_000),
-              dict(kernel="dedup", n=2, layer=0, U=15, bytes=1_000_000)]
+    passes = [dict(workload="qwen3x48", kernel="slot", n=1, layer=0, U=8, bytes=2_000_000),
+              dict(workload="tree", kernel="slot", n=32, layer=0, U=15, bytes=6_000_000),
+              dict(workload="qwen3x48", kernel="dedup", n=1, layer=0, U=8, bytes=1_000_000)]
     log = tmp_path / "pmc.log"
     log.write_text("noise\n" + json.dumps({"pmc_pass": passes, "source_hash": "abc"}) + "\n")
     path = bench.write_traffic_summary(fp, wp, str(log), out_dir=str(tmp_path))
     rec = json.loads([l for l in open(path) if l.startswith("traffic-json: ")][0][len("traffic-json: "):])
-    assert rec["source_hash"] == "abc" and rec["slot_launches"] == 2 and rec["dedup_launches"] == 1
-    assert rec["slot_bytes_per_launch"] == ((1000 + 3000) * 2 + (4 + 8)) * 1024 / 2
-    assert rec["slot_algorithmic_bytes_per_launch"] == 4_000_000
-    assert rec["dedup_bytes_per_launch"] == (500 * 2 + 2) * 1024
-    assert rec["dedup_algorithmic_bytes_per_launch"] == 1_000_000
+    assert rec["source_hash"] == "abc"
+    q, t = rec["per_launch"]["qwen3x48"], rec["per_launch"]["tree"]
+    assert q["slot"]["launches"] == 1 and t["slot"]["launches"] == 1 and q["dedup"]["launches"] == 1
+    assert q["slot"]["bytes"] == (1000 * 2 + 4) * 1024 and t["slot"]["bytes"] == (3000 * 2 + 8) * 1024
+    assert q["slot"]["algorithmic"] == 2_000_000 and q["slot"]["fetched_over_algorithmic"] == round(
+        1000 * 2 * 1024 / 2_000_000, 4)
+    assert q["dedup"]["bytes"] == (500 * 2 + 2) * 1024 and q["dedup"]["algorithmic"] == 1_000_000
+    assert "tree" in open(path).read()
 
 
 def test_cpu_baseline_one_thread_and_all_cores():
