@@ -110,3 +110,54 @@ def assert_close(y, ref, what=""):
     assert np.all(np.isfinite(y)), what
     assert rel <= REL_L2_TOL and mx <= MAX_ABS_TOL, "%s rel_l2=%.3e max_abs=%.3e" % (what, rel, mx)
     return rel, mx
+
+
+class TorchGenLayer:
+    """A full-size layer whose plain weights are drawn on the device by the seeded
+    device generator (``synth.device.device_layer_weights``); the kernels run on the
+    copies the library's packing kernels make (``layouts``), the oracle on the plain
+    weights of the experts a pass touches, copied to the host."""
+
+    def __init__(self, spec, seed, layer=0, layouts=("tiled",), keep_plain=True):
+        from synth.device import device_layer_weights
+        self.spec = spec
+        w = device_layer_weights(spec, seed, layer)
+        plain = efa.Layer(*w, m=spec.m)
+        self.devs = {}
+        for lay in layouts:
+            self.devs[lay] = plain if lay == "plain" else (plain.tiled_copy() if lay == "tiled" else plain.packed_copy())
+        self.plain = w if keep_plain else None
+        self._host = {}
+        torch.cuda.synchronize()
+
+    def host_experts(self, experts):
+        """(W_gate, W_up, W_down) bf16 bit patterns of the listed experts, [E'][...]."""
+        from synth.device import from_torch_bf16
+        idx = torch.as_tensor(np.asarray(experts, np.int64), device="cuda")
+        return tuple(from_torch_bf16(t.index_select(0, idx)) for t in self.plain)
+
+    def oracle_tasks(self, passes):
+        """Arguments of one oracle call per pass (x_host, ids, w), on the experts the
+        passes touch only (copied once; each pass's ids renumbered into them)."""
+        ex = np.unique(np.concatenate([np.asarray(ids, np.int32).reshape(-1) for _, ids, _ in passes]))
+        W = self.host_experts(ex)
+        return [(W, np.ascontiguousarray(x), np.searchsorted(ex, np.asarray(ids, np.int32)).astype(np.int32),
+                 np.ascontiguousarray(w, np.float32)) for x, ids, w in passes]
+
+
+def oracle_many(tasks, threads=16):
+    """oracle.moe_ffn over many (weights, x, ids, w) tasks on a thread pool (the C call
+    releases the GIL); results in task order."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(threads) as pool:
+        return list(pool.map(lambda t: oracle.moe_ffn(*t[0], t[1], t[2], t[3], "bf16"), tasks))
+
+
+def run_pair(layer, x, ids, w, ws, y_slot=None, y_dedup=None):
+    """Both kernels on one pass (device tensors) through the C ABI; returns their
+    outputs and info words (U, ids status, sync status)."""
+    info_s = torch.full((3,), 99, dtype=torch.int32, device="cuda")
+    info_d = torch.full((3,), 99, dtype=torch.int32, device="cuda")
+    ys = efa.expert_perslot(layer, x, ids, w, y=y_slot, ws=ws, info=info_s)
+    yd = efa.expert_dedup(layer, x, ids, w, y=y_dedup, ws=ws, info=info_d)
+    return ys, yd, info_s, info_d

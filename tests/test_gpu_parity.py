@@ -123,8 +123,9 @@ def test_pack_tiled_bit_exact(dtype, E, R, K, mat):
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_tiny_fp32_many_seeds(layout):
     spec = synth.CONFIGS["tiny"]
-    for seed in range(30 if layout == "plain" else 10):
-        say("tiny seed", seed, "layout", layout)
+    for seed in range(1000):
+        if seed % 100 == 0:
+            say("tiny seeds", seed, "..", seed + 99, "layout", layout)
         dl = DeviceLayer(spec, seed, layout=layout)
         tr = routing.uniform_trace(spec.N, spec.m, 4, routing.rng_for(seed, 0, "uniform"))
         x = synth.pass_x(spec, seed, 0, 0, 4)
@@ -320,21 +321,8 @@ def test_qwen3_layer_zipf_and_tree(layout):
         _compare(dl, x, ids, w, "qwen3 n=%d" % n)
     parents, ttr = routing.tree_routing(spec.N, spec.m, 0.5, routing.rng_for(77, 3, "tree"))
     x = synth.pass_x(spec, 77, 3, 500, 32)
-    say("tree pass n=32")
-    _compare(dl, x, ttr.ids, ttr.w, "tree", tokens=[0, 1, 7, 19, 31])
-
-
-@pytest.mark.parametrize("layout", LAYOUTS)
-def test_mixtral_sampled_tokens(layout):
-    spec = synth.CONFIGS["mixtral"]
-    say("upload mixtral layer", "layout", layout)
-    dl = DeviceLayer(spec, 9, layout=layout)
-    tr = routing.make_trace(spec, "correlated", 64, seed=9, p=0.6)
-    for n, toks in ((1, [0]), (3, [0, 2]), (8, [1, 6])):
-        ids, w = routing.window(tr, 10, n)
-        x = synth.pass_x(spec, 9, 0, n, n)
-        say("mixtral n", n, "tokens", toks)
-        _compare(dl, x, ids, w, "mixtral n=%d" % n, tokens=toks)
+    say("tree pass n=32, every token")
+    _compare(dl, x, ttr.ids, ttr.w, "tree")
 
 
 @pytest.mark.parametrize("kind", ["uniform", "correlated"])
