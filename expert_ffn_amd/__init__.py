@@ -9,6 +9,7 @@ from ._abi import (  # noqa: F401
     MOE_KIND_DEDUP, MOE_KIND_SLOT, MOE_MAT_DOWN, MOE_MAT_GATE_UP, MoeError, lib,
 )
 from .ops import (  # noqa: F401
-    Grouping, Layer, bytes_requested, error_bounds, expert_auto, expert_bitmaps, expert_dedup, expert_perslot, fit_times,
-    kernels_per_call, pack_tiled, pack_w_down, route_group, router_topk, step_time_model, tree_select,
+    Grouping, Layer, bytes_requested, error_bounds, expert_auto, expert_auto_noalloc, expert_bitmaps, expert_dedup,
+    expert_perslot, fit_times, kernels_per_call, pack_tiled, pack_w_down, route_group, router_topk, step_time_model,
+    tree_select,
 )

@@ -19,6 +19,7 @@ MOE_FLAG_WDOWN_PACKED = 2
 MOE_FLAG_TILED = 4
 MOE_MAT_GATE_UP, MOE_MAT_DOWN = 0, 1
 MOE_STEP_NMAX, MOE_STEP_AMAX = 16, 64
+MOE_SCRATCH_BYTES = 16 << 20
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_E_INVAL", -2: "MOE_E_DTYPE", -3: "MOE_E_WORKSPACE",
                 -4: "MOE_E_HIP", -5: "MOE_E_IDS"}
@@ -28,7 +29,7 @@ EXPORTS = ("moe_route_group", "moe_workspace_bytes", "moe_expert_perslot", "moe_
            "moe_kernels_per_call", "moe_expert_perslot_ev", "moe_expert_dedup_ev", "bytes_requested",
            "step_time_model", "moe_pack_w_down", "moe_fit_times", "moe_error_bounds",
            "moe_router_topk", "moe_router_workspace_bytes", "moe_tree_select",
-           "moe_expert_auto", "moe_pack_tiled")
+           "moe_expert_auto", "moe_pack_tiled", "moe_expert_auto_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -134,6 +135,8 @@ def lib():
             L.moe_tree_select.restype = ctypes.c_int
             L.moe_expert_auto.argtypes = [pdesc, pw, vp, vp, vp, i32, vp, vp, vp, sz, i32, vp, vp]
             L.moe_expert_auto.restype = ctypes.c_int
+            L.moe_expert_auto_noalloc.argtypes = [pdesc, pw, vp, vp, vp, i32, vp, vp, i32, vp, vp]
+            L.moe_expert_auto_noalloc.restype = ctypes.c_int
             _LIB = L
     return _LIB
 

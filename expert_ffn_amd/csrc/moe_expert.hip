@@ -7,9 +7,17 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "expert_kernel.h"
 #include "moe_expert.h"
+
+// Workspace of moe_expert_auto_noalloc: one copy per GPU, in the code object's
+// device memory.  In host code `scratch` names a host-side stand-in, not the
+// device array: host code uses only the address hipGetSymbolAddress returns for
+// the current device (scratch_of_current_device).
+static __device__ __align__(256) char scratch[MOE_SCRATCH_BYTES];
 
 namespace {
 
@@ -463,10 +471,15 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     return p;
 }
 
+// Zeroes `words` int32 words (the counter area at the start of a workspace).
+__global__ __launch_bounds__(256) void k_zero_words(int32_t* __restrict__ p, int words) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < words; i += gridDim.x * 256) p[i] = 0;
+}
+
 template <int MODE>
 int run_expert(const moe_layer_desc* d, const moe_layer_weights* W, const void* x, const int32_t* ids,
                const float* w, int32_t n, float* y, int32_t* info, void* ws, size_t ws_bytes, void* stream,
-               void* const* events, int32_t n_events) {
+               void* const* events, int32_t n_events, bool clear_counters = false) {
     int rc = check_desc(d, n);
     if (rc != MOE_OK) return rc;
     if (!W || !W->w_gate || !W->w_up || !W->w_down || !x || !ids || !w || !y || !ws) return MOE_E_INVAL;
@@ -520,6 +533,9 @@ int run_expert(const moe_layer_desc* d, const moe_layer_weights* W, const void* 
     args.part = reinterpret_cast<float*>(wsb + p.part_off);
     const int grid = p.g1 + p.units * p.T2 * p.ks;
     (void)hipGetLastError();
+    if (clear_counters)  // a workspace whose counters may not be zero (a shared array): clear them first
+        hipLaunchKernelGGL(k_zero_words, dim3((kSyncWords + 255) / 256), dim3(256), 0, st,
+                           reinterpret_cast<int32_t*>(wsb + p.sync_off), kSyncWords);
     if (events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(events[0]), st);
     const bool bf = d->dtype == MOE_BF16;
     const int lay = (d->flags & MOE_FLAG_TILED) ? kLayTiled : (d->flags & MOE_FLAG_WDOWN_PACKED) ? kLayPacked : kLayPlain;
@@ -537,6 +553,35 @@ int router_ks(const moe_layer_desc* d, int32_t n) {
     const int wg = ((d->N + kTile - 1) / kTile) * ((n + kTile - 1) / kTile);
     const int steps = (d->d_model + (d->dtype == MOE_BF16 ? 32 : 16) - 1) / (d->dtype == MOE_BF16 ? 32 : 16);
     return std::max(1, std::min(std::min(kRKS, kCUs / wg), steps / kWaves));
+}
+
+// ---------------------------------------------------------------------------
+// moe_expert_auto_noalloc: the scratch array's device address, once per device
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_of_current_device(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_E_HIP;
+    if (stream) {  // the array used is the current device's: the stream must be on it
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MOE_E_HIP;
+        if ((int)sdev != dev) return MOE_E_INVAL;
+    }
+    if (dev >= kMaxDevices) return MOE_E_HIP;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_E_HIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MOE_OK;
 }
 
 int router_check(const moe_layer_desc* desc, int32_t n) {
@@ -684,6 +729,29 @@ int moe_expert_auto(const moe_layer_desc* desc, const moe_layer_weights* weights
     const int rc = dedup ? run_expert<kDedup>(desc, weights, x, ids, w, n, y, info, ws, ws_bytes, hip_stream, nullptr, 0)
                          : run_expert<kPerSlot>(desc, weights, x, ids, w, n, y, info, ws, ws_bytes, hip_stream, nullptr,
                                                 0);
+    if (rc == MOE_OK && kind_out) *kind_out = dedup ? MOE_KIND_DEDUP : MOE_KIND_SLOT;
+    return rc;
+}
+
+int moe_expert_auto_noalloc(const moe_layer_desc* desc, const moe_layer_weights* weights, const void* x,
+                            const int32_t* ids, const float* w, int32_t n, float* y, int32_t* info,
+                            int32_t crossover, int32_t* kind_out, void* hip_stream) {
+    if (crossover < 0) return MOE_E_INVAL;
+    int rc = check_desc(desc, n);
+    if (rc != MOE_OK) return rc;
+    const bool dedup = crossover > 0 && n >= crossover;
+    if (plan_for(desc, n, dedup ? MOE_KIND_DEDUP : MOE_KIND_SLOT).total > (size_t)MOE_SCRATCH_BYTES)
+        return MOE_E_WORKSPACE;
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    void* ws = nullptr;
+    rc = scratch_of_current_device(st, &ws);
+    if (rc != MOE_OK) return rc;
+    // the expert call validates every argument, then clears the array's counter
+    // words (a kernel on the same stream) and launches
+    rc = dedup ? run_expert<kDedup>(desc, weights, x, ids, w, n, y, info, ws, MOE_SCRATCH_BYTES, hip_stream, nullptr, 0,
+                                    true)
+               : run_expert<kPerSlot>(desc, weights, x, ids, w, n, y, info, ws, MOE_SCRATCH_BYTES, hip_stream,
+                                      nullptr, 0, true);
     if (rc == MOE_OK && kind_out) *kind_out = dedup ? MOE_KIND_DEDUP : MOE_KIND_SLOT;
     return rc;
 }

@@ -270,6 +270,28 @@ def expert_auto(layer, x, ids, w, crossover, y=None, ws=None, info=None, accumul
     return y, kind.value
 
 
+def expert_auto_noalloc(layer, x, ids, w, crossover, y=None, info=None, accumulate=False, stream=None):
+    """``moe_expert_auto_noalloc``: the same switch with no workspace argument (the
+    library's per-GPU scratch array serves as workspace; nothing is allocated by the
+    call itself).  Returns (y, kind run).  ``y`` should be preallocated by callers
+    that cannot allocate."""
+    n = x.shape[0]
+    _check_dev("x", x, layer.dtype, (n, layer.d))
+    _check_dev("ids", ids, torch.int32, (n, layer.m))
+    _check_dev("w", w, torch.float32, (n, layer.m))
+    if y is None:
+        y = torch.empty(n, layer.d, dtype=torch.float32, device=x.device)
+    _check_dev("y", y, torch.float32, (n, layer.d))
+    if info is not None:
+        _check_dev("info", info, torch.int32, (3,))
+    desc = layer.desc(accumulate)
+    kind = ctypes.c_int32(-1)
+    st = lib().moe_expert_auto_noalloc(ctypes.byref(desc), ctypes.byref(layer._weights), _vp(x), _vp(ids), _vp(w), n,
+                                       _vp(y), _vp(info), int(crossover), ctypes.byref(kind), _stream(stream))
+    check("moe_expert_auto_noalloc", st)
+    return y, kind.value
+
+
 def kernels_per_call(kind):
     return lib().moe_kernels_per_call(int(kind))
 

@@ -193,6 +193,31 @@ int moe_expert_auto(const moe_layer_desc* desc, const moe_layer_weights* weights
                     void* hip_stream);
 
 /*
+ * moe_expert_auto_noalloc -- moe_expert_auto with no workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The kernels' workspace (counters, h, O,
+ * partial sums) is a file-scope device array of MOE_SCRATCH_BYTES in the library,
+ * one per GPU, held until the process ends.  Nothing is allocated: no hipMalloc,
+ * hipFree or allocating library routine is called.
+ *   Arguments as for moe_expert_auto, minus ws and ws_bytes.  The current device must
+ *   be the device of hip_stream (the array used is the current device's).
+ *   Each call first clears the array's counter words with a small kernel on
+ *   hip_stream (a kernel, not a memset, so a graph capture records a kernel node),
+ *   then runs the kernel moe_expert_auto would run: two launches per call.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ *   (on different streams, or from different threads without ordering) race and
+ *   their results are undefined.  Calls on one stream are ordered and safe.
+ * Returns what moe_expert_auto returns; MOE_E_WORKSPACE (nothing enqueued) when the
+ * pass needs more than MOE_SCRATCH_BYTES (moe_workspace_bytes of the kernel that
+ * would run); MOE_E_INVAL when the stream's device is not the current device;
+ * MOE_E_HIP when the array's address cannot be obtained.
+ */
+#define MOE_SCRATCH_BYTES (16u << 20)
+int moe_expert_auto_noalloc(const moe_layer_desc* desc, const moe_layer_weights* weights, const void* x,
+                            const int32_t* ids, const float* w, int32_t n, float* y, int32_t* info,
+                            int32_t crossover, int32_t* kind_out, void* hip_stream);
+
+/*
  * moe_pack_w_down -- copy W_down [N][d_model][d_ff] into the packed layout
  * [N][d_ff/8][d_model][8]: element (e, i, f) goes to
  *     ((e*(d_ff/8) + f/8)*d_model + i)*8 + f%8,
