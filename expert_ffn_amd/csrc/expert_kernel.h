@@ -261,6 +261,7 @@ struct Args {
     int32_t gl;          // down items in register mode: tokens of h staged in LDS at a time
     int32_t g1;          // gate/up work groups (they take the first g1 block ids)
     int32_t S1;          // K steps of one gate/up row tile
+    int32_t split_ok;    // the workspace holds the partial sums of split gate/up tiles
     float* part;         // split gate/up tiles: partial sums [kMaxContrib][nslot][d_ff][gate, up]
 };
 
@@ -277,21 +278,20 @@ struct Smem {
     int32_t grp[MOE_MAX_SLOTS];    // slots of this workgroup's unit, increasing
     uint32_t pres[MOE_MAX_EXPERTS / 32];
     int32_t id_status;             // set for ids out of range or repeated within a token
+    float cw[MOE_MAX_SLOTS];       // down items: routing weight of each slot, for the combine
+    int32_t cok[MOE_MAX_SLOTS];    // down items: the slot's id is in range
 };
 
-// Stable grouping of the pass's slots by expert, in LDS, for distinct expert
-// number `u` (ids in increasing order): returns e (or -1 when u >= U), g and U, and
-// with `group` writes the unit's slots, increasing, to sm.grp[0..g).  Every wave
-// computes the presence scan and the ranks itself (and writes all of sm.grp), so
-// no barrier is needed after it.  With want_status, sm.id_status is set for ids out
-// of range or repeated within a token (read after the call by thread 0).
+// The pass's ids in LDS (ids out of range as -1) and the presence bitmap of the
+// experts they name; with want_status, sm.id_status is set for ids out of range or
+// repeated within a token (read after the call by thread 0).  Loaded once per work
+// group: the unit selections below read it.  Starts and ends with a barrier.
 template <int NB>
-__device__ void group_prologue(const Args& a, Smem<NB>& sm, int u, bool want_status, bool group, int& e_out,
-                               int& g_out, int& U_out) {
-    const int tid = threadIdx.x, lane = tid & 63;
+__device__ void load_ids(const Args& a, Smem<NB>& sm, bool want_status) {
+    const int tid = threadIdx.x;
     const int nm = a.n * a.m;
     const int nwords = (a.N + 31) >> 5;
-    __syncthreads();  // the previous unit's reads of sm are done
+    __syncthreads();  // earlier reads of sm are done
     if (tid < nwords) sm.pres[tid] = 0u;
     if (tid == 0) sm.id_status = 0;
     const int id = tid < nm ? a.ids[tid] : -1;
@@ -308,6 +308,21 @@ __device__ void group_prologue(const Args& a, Smem<NB>& sm, int u, bool want_sta
         if (bad) atomicOr(&sm.id_status, 1);
     }
     __syncthreads();
+}
+
+// Stable grouping of the pass's slots by expert, from what load_ids left in LDS: the
+// number U of distinct experts and, for distinct expert number `u` (ids in increasing
+// order; u < 0 or u >= U: none), its id e (else -1) and, with `group`, its slots,
+// increasing, in sm.grp[0..g).  Every wave computes the prefix popcount and the
+// ranks itself (and writes all of sm.grp), so no barrier is needed after it; the
+// barrier before it keeps the previous unit's reads of sm.grp ahead of the writes.
+template <int NB>
+__device__ void select_unit(const Args& a, Smem<NB>& sm, int u, bool group, int& e_out, int& g_out, int& U_out,
+                            bool barrier = true) {
+    const int lane = threadIdx.x & 63;
+    const int nm = a.n * a.m;
+    const int nwords = (a.N + 31) >> 5;
+    if (barrier) __syncthreads();
     // prefix popcount over the presence words (<= 32 words, lanes 0..31)
     const uint32_t word = lane < nwords ? sm.pres[lane] : 0u;
     const int c = __popc(word);
@@ -342,6 +357,27 @@ __device__ void group_prologue(const Args& a, Smem<NB>& sm, int u, bool want_sta
     e_out = e;
     g_out = g;
     U_out = U;
+}
+
+// Gate/up work groups for `tiles` row tiles of S1 K steps: the (unit, tile, K step)
+// space is cut into kCUs equal shares when there are between half the compute units
+// and `upper` tiles, each tile into two shares when there are fewer than half (and K
+// has two steps), else one work group per tile; `split_ok` false forbids cutting (no
+// room for partial sums).  Non-decreasing in `tiles` (upper >= kCUs).
+// upper: 2 kCUs for the per-slot kernel, kDedupSplitUpper for the deduplicating one.
+// Same box, Qwen3-shaped layer x48 (zipf) and DeepSeek-V2-Lite-shaped layer, 8 windows
+// per n, two rounds agreeing within 0.1 us: the deduplicating kernel is 1-4 us per
+// layer faster at n = 3..8 and 0.9-3 us at n = 2 when it cuts only below 288 tiles
+// (against 320, 384, 512); the per-slot kernel's 384-tile pass (Qwen3 shape, n = 2)
+// is 3.2 us faster cut (29.8 against 33.0 us).  A work group's own stream is bounded
+// by the loads it keeps in flight, so one work group per tile keeps more bytes in
+// flight; below ~288 tiles the compute units with two tiles finish last by a whole
+// tile, and the cut wins.
+constexpr int kDedupSplitUpper = 288;
+__host__ __device__ inline int gate_up_groups(int tiles, int S1, bool split_ok, int upper) {
+    const bool few = tiles * 2 < kCUs && S1 >= 2;
+    const bool split = ((tiles * 2 >= kCUs && tiles < upper) || few) && split_ok;
+    return !split ? tiles : (few ? 2 * tiles : kCUs);
 }
 
 // Bounded wait until *p >= target (one thread).  Returns false on expiry.
@@ -595,37 +631,56 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so step offsets are scalar
     const int lr = lane & 15, q = lane >> 4;
     const int nm = a.n * a.m;
-    const bool phase1 = (int)blockIdx.x < a.g1;
     const bool want_status = a.info != nullptr && blockIdx.x == 0;
 
-    // The unit u: expert e and its slots sm.grp[0..g); sh: e is a shared expert (all
-    // n tokens, weight 1, slots nm + e*n + t).  `status`: also report U and the ids'
-    // status (work group 0).
-    auto resolve = [&](int u, bool status, int& e, int& g, bool& sh) {
-        sh = SH && u >= a.units_r;
-        if ((MODE == kDedup && !sh) || status) {
-            int U;
-            group_prologue<NT * RB>(a, sm, MODE == kDedup && !sh ? u : 0, status, MODE == kDedup && !sh, e, g, U);
-            if (status && tid == 0) {
-                a.info[0] = U;
-                a.info[1] = sm.id_status ? MOE_E_IDS : MOE_OK;
-                a.info[2] = MOE_OK;  // a bounded wait that expires later overwrites this
-            }
+    // The pass's units and gate/up work groups.  The per-slot kernel's are the
+    // host's (one unit per slot).  The deduplicating kernel's real units, one per
+    // distinct expert, are known on the device only: the host sized the grid for
+    // min(n m, N) routed units, and every work group counts the U distinct experts
+    // (the ids are loaded once into LDS) and takes its role among U routed units
+    // (at least one, so a pass without valid ids still writes y) and the shared
+    // experts: gate/up shares over their tiles (gate_up_groups is non-decreasing, so
+    // they never outnumber the host's), then their down items, and the work groups
+    // left over at the end of the grid exit.
+    int units = a.units, units_r = a.units_r, g1 = a.g1;
+    if (MODE == kDedup || want_status) {
+        load_ids<NT * RB>(a, sm, want_status);
+        int e_, g_, U;
+        select_unit<NT * RB>(a, sm, -1, false, e_, g_, U, false);  // (load_ids ended with a barrier)
+        U = uni(U);
+        if (MODE == kDedup) {
+            units_r = max(U, 1);
+            units = units_r + (SH ? a.n_shared : 0);
+            g1 = gate_up_groups(units * a.T1, a.S1, a.split_ok, kDedupSplitUpper);
         }
+        if (want_status && tid == 0) {
+            a.info[0] = U;
+            a.info[1] = sm.id_status ? MOE_E_IDS : MOE_OK;
+            a.info[2] = MOE_OK;  // a bounded wait that expires later overwrites this
+        }
+    }
+    const bool phase1 = (int)blockIdx.x < g1;
+
+    // The unit u: expert e and its slots sm.grp[0..g); sh: e is a shared expert (all
+    // n tokens, weight 1, slots nm + e*n + t).
+    auto resolve = [&](int u, int& e, int& g, bool& sh) {
+        sh = SH && u >= units_r;
         if (sh) {
-            e = u - a.units_r;
+            e = u - units_r;
             g = a.n;
             __syncthreads();  // the previous unit's reads of sm.grp are done
             if (tid < a.n) sm.grp[tid] = nm + e * a.n + tid;
             __syncthreads();
         } else if (MODE == kDedup) {
+            int U;
+            select_unit<NT * RB>(a, sm, u, true, e, g, U);
             e = uni(e);
             g = uni(g);
         } else {
             const int id = uni(a.ids[u]);
             e = (id >= 0 && id < a.N) ? id : -1;
             g = e >= 0 ? 1 : 0;
-            if (tid == 0) sm.grp[0] = u;
+            if (tid == 0) sm.grp[0] = u;  // (gate_up ends with a barrier after its last read of sm.grp)
             __syncthreads();
         }
     };
@@ -638,8 +693,8 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) 
         // Without a split, work group wi holds tile wi whole.  With one, the
         // products below stay under 2^31: at most kMaxSplitTiles tiles and
         // g1 <= kMaxSplitTiles.
-        const int tiles = a.units * a.T1;
-        const bool split = a.g1 != tiles;
+        const int tiles = units * a.T1;
+        const bool split = g1 != tiles;
         const int ltot = tiles * a.S1;
         const int wi = blockIdx.x;
         // (integer divisions run on the vector unit: readfirstlane keeps the
@@ -648,30 +703,30 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) 
         // of a split tile (it contributes without waiting) and its first is the
         // tail of one (it finalises, waiting on lower work-group ids).  In this
         // order no wait depends on another wait.
-        const int lbeg = uni(split ? wi * ltot / a.g1 : wi * a.S1);
+        const int lbeg = uni(split ? wi * ltot / g1 : wi * a.S1);
         int cur = -1, e = -1, g = 0;
         bool sh = false;
-        for (int L = uni(split ? (wi + 1) * ltot / a.g1 : (wi + 1) * a.S1); L > lbeg;) {
+        for (int L = uni(split ? (wi + 1) * ltot / g1 : (wi + 1) * a.S1); L > lbeg;) {
             const int tile = uni((L - 1) / a.S1);
             const int k1 = L - tile * a.S1;
             const int k0 = max(0, lbeg - tile * a.S1);
             L = tile * a.S1 + k0;
             const int u = uni(tile / a.T1), t = tile - u * a.T1;
             if (u != cur) {
-                resolve(u, want_status && cur < 0, e, g, sh);
+                resolve(u, e, g, sh);
                 cur = u;
             }
             if (g == 0) continue;
             // work groups whose shares meet this tile: first .. last
-            const int first = uni(split ? ((tile * a.S1 + 1) * a.g1 - 1) / ltot : wi);
-            const int last = uni(split ? ((tile * a.S1 + a.S1) * a.g1 - 1) / ltot : wi);
+            const int first = uni(split ? ((tile * a.S1 + 1) * g1 - 1) / ltot : wi);
+            const int last = uni(split ? ((tile * a.S1 + a.S1) * g1 - 1) / ltot : wi);
             const bool fin = gate_up<BF16, NT, RB, KF, P, SH, TL>(a, sm, e, sh, g, t, k0, k1, tile,
                                                               last - first + 1, wi - first);
             if (tid == 0 && fin) atomicAdd(a.sync + kLine * u, 1);  // h-ready count of unit u
         }
-        if (want_status && cur < 0) resolve(0, true, e, g, sh);  // an empty share still reports the status
     } else {
-        const int item = (int)blockIdx.x - a.g1;
+        const int item = (int)blockIdx.x - g1;
+        if (item >= units * a.T2 * a.ks) return;  // deduplicating kernel: a work group with no role
         const int ut = item / a.ks, kp = item - ut * a.ks;  // contraction part kp of (unit, row tile)
         const int u = ut / a.T2, t = ut - u * a.T2;
         int32_t* hcnt = a.sync + kLine * u;      // this unit's h-ready count
@@ -679,7 +734,15 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) 
         int32_t* ocnt = a.sync + kLine * (MOE_MAX_SLOTS + t);  // arrivals on this down tile
         int e, g;
         bool sh;
-        resolve(u, false, e, g, sh);
+        resolve(u, e, g, sh);
+        // the slots' routing weights and id validity for the combine, loaded now (their
+        // latency hidden behind this item's work; read after the barrier that follows
+        // the arrival) so that a combining work group issues its O loads at once
+        if (tid < nm) {
+            const int id = a.ids[tid];
+            sm.cok[tid] = (id >= 0 && id < a.N) ? 1 : 0;
+            sm.cw[tid] = a.w[tid];
+        }
         // ================ down: O for RT2 rows of d ================
         if (g > 0) {
             const uint32_t mat = (uint32_t)a.d * a.d_ff * F::kEsize;
@@ -885,7 +948,7 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) 
         // arrival on this row tile; the last unit to arrive combines its rows
         if (tid == 0) {
             const int old = atomicAdd(ocnt, 1);  // after the writers' completed stores and the barrier
-            s_last = old == a.units * a.ks - 1;
+            s_last = old == units * a.ks - 1;
             if (s_last) __hip_atomic_store(ocnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // all arrived
         }
         __syncthreads();  // O loads (sc1) below are issued after the last arrival was seen
@@ -916,10 +979,9 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) 
                         float wgt = 1.f;
                         if (c < nr) {
                             const int s = tok * a.m + c / ks;
-                            const int id = a.ids[s];
-                            if (id >= 0 && id < a.N) {
+                            if (sm.cok[s]) {
                                 sl = s;
-                                wgt = a.w[s];
+                                wgt = sm.cw[s];
                             }
                         } else if (SH && c < npair) {
                             sl = nm + ((c - nr) / ks) * a.n + tok;
@@ -935,7 +997,8 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) 
                             for (int r = 0; r < 4; ++r) acc[r] = fmaf(wv[jj], __uint_as_float(ov[jj][r]), acc[r]);
                 }
                 f32x4* yp = reinterpret_cast<f32x4*>(a.y + (size_t)tok * a.d + i);
-                *yp = a.accumulate ? *yp + acc : acc;
+                if (a.accumulate) acc += *yp;  // y is read only when the call accumulates
+                *yp = acc;
             }
         }
     }
@@ -944,6 +1007,7 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) 
 struct Plan {
     int units, units_r, nslot, T1, T2, nt, rb, ks;
     int g1, S1;  // gate/up work groups, K steps per gate/up tile
+    bool split_ok;  // the workspace holds partial sums of split gate/up tiles
     size_t part_off;
     int dpf;     // down items: 0 streaming, 1 register mode (16 rows), 2 register mode (32 rows)
     int gl;      // register mode: tokens of h staged in LDS at a time

@@ -412,20 +412,24 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     p.T1 = (d->d_ff + kTile * p.rb - 1) / (kTile * p.rb);
     const bool bf = d->dtype == MOE_BF16;
     const int es = bf ? 2 : 4, step = 64 / es;  // bytes per element, elements per K step
-    // Gate/up work is cut into kCUs equal shares when there are between half and
-    // twice as many tiles as compute units: then no compute unit holds two tiles
-    // while another holds one.  With fewer tiles than half the compute units (a
-    // pass of one or two experts), every tile is cut in two, so twice as many
-    // compute units stream (a compute unit's own stream is bounded by the loads
-    // it keeps in flight).  Each share is at least half a tile, so a tile is
-    // shared by at most kMaxContrib work groups.  Otherwise one work group per
-    // tile (with more tiles, cutting them measured slower than the imbalance).
+    // Gate/up work is cut into kCUs equal shares when there are between half the
+    // compute units and an upper bound of tiles (2 kCUs per-slot, kDedupSplitUpper
+    // deduplicating): then no compute unit holds two tiles while another holds one.
+    // With fewer tiles than half the compute units (a pass of one or two experts),
+    // every tile is cut in two, so twice as many compute units stream (a compute
+    // unit's own stream is bounded by the loads it keeps in flight).  Each share is
+    // at least half a tile, so a tile is shared by at most kMaxContrib work groups.
+    // Otherwise one work group per tile (with more tiles, cutting them measured
+    // slower than the imbalance).
+    // (gate_up_groups; the deduplicating kernel applies the same rule on the device
+    // to its real units, U of the min(n m, N) planned here, and may cut tiles where
+    // this plan does not: its workspace always holds the partial sums)
     p.S1 = (d->d_model + step - 1) / step;
     const int64_t tiles = (int64_t)p.units * p.T1;
     const int64_t part_bytes = (int64_t)kMaxContrib * p.nslot * d->d_ff * 8;
-    const bool few = tiles * 2 < kCUs && p.S1 >= 2;
-    const bool split = ((tiles * 2 >= kCUs && tiles < 2 * kCUs) || few) && part_bytes <= (64ll << 20);
-    p.g1 = !split ? (int)tiles : (few ? (int)(2 * tiles) : kCUs);
+    p.split_ok = part_bytes <= (64ll << 20);
+    p.g1 = gate_up_groups((int)tiles, p.S1, p.split_ok, kind == MOE_KIND_SLOT ? 2 * kCUs : kDedupSplitUpper);
+    const bool split = p.g1 != tiles;
     // Down items in register mode: when a wave's share of the down contraction fits
     // kPF steps, and one LDS chunk of at most 16 tokens (one MFMA column tile) holds a
     // whole group (several chunks would serialise their h loads and O stores; a
@@ -467,7 +471,7 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     p.h_off = (size_t)kSyncWords * 4;
     p.o_off = p.h_off + align_up((size_t)p.nslot * d->d_ff * 4);
     p.part_off = p.o_off + align_up((size_t)p.nslot * p.ks * d->d_model * 4);
-    p.total = p.part_off + (split ? align_up((size_t)part_bytes) : 0);
+    p.total = p.part_off + ((split || (kind == MOE_KIND_DEDUP && p.split_ok)) ? align_up((size_t)part_bytes) : 0);
     return p;
 }
 
@@ -530,6 +534,7 @@ int run_expert(const moe_layer_desc* d, const moe_layer_weights* W, const void* 
     args.gl = p.gl;
     args.g1 = p.g1;
     args.S1 = p.S1;
+    args.split_ok = p.split_ok ? 1 : 0;
     args.part = reinterpret_cast<float*>(wsb + p.part_off);
     const int grid = p.g1 + p.units * p.T2 * p.ks;
     (void)hipGetLastError();
