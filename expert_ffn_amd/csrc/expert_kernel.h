@@ -262,6 +262,7 @@ struct Args {
     int32_t g1;          // gate/up work groups (they take the first g1 block ids)
     int32_t S1;          // K steps of one gate/up row tile
     int32_t split_ok;    // the workspace holds the partial sums of split gate/up tiles
+    int32_t reg_wgs;     // deduplicating kernel: most work groups (gate/up and down) for register-mode down items
     float* part;         // split gate/up tiles: partial sums [kMaxContrib][nslot][d_ff][gate, up]
 };
 
@@ -378,6 +379,23 @@ __host__ __device__ inline int gate_up_groups(int tiles, int S1, bool split_ok, 
     const bool few = tiles * 2 < kCUs && S1 >= 2;
     const bool split = ((tiles * 2 >= kCUs && tiles < upper) || few) && split_ok;
     return !split ? tiles : (few ? 2 * tiles : kCUs);
+}
+
+// Down items of a pass of `units` units whose gate/up work takes g1 work groups: in
+// register mode (rbr row blocks an item, the whole d_ff contraction) when it is
+// allowed and the pass's work groups, the g1 and these items, number at most
+// reg_wgs (about 11/4 rounds of what the compute units hold at once); else
+// streaming (rbs row blocks an item), the d_ff contraction of each (unit, row tile)
+// cut into ks_s parts.
+constexpr int kMaxKs = 4;  // contraction parts of a streaming down item, at most
+struct DownShape {
+    int reg, T2, ks;
+};
+__host__ __device__ inline DownShape down_shape(int units, int g1, int d, bool reg_allowed, int rbr, int rbs,
+                                                int reg_wgs, int ks_s) {
+    const int t2r = (d + kTile * rbr - 1) / (kTile * rbr);
+    if (reg_allowed && g1 + units * t2r <= reg_wgs) return DownShape{1, t2r, 1};
+    return DownShape{0, (d + kTile * rbs - 1) / (kTile * rbs), ks_s};
 }
 
 // Bounded wait until *p >= target (one thread).  Returns false on expiry.
@@ -600,6 +618,305 @@ __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e,
 constexpr int kPF = 12;
 constexpr int kSL = 4;  // register mode: h staging loads in flight per thread
 
+// ---------------------------------------------------------------------------
+// One down work group: item `item` of the pass's units * T2 * ks down items, O for
+// RT2 rows of d of one unit (or one contraction part of them), then its arrival on
+// the row tile and, for the last unit to arrive, the combine.  DPF > 0: register
+// mode (RBR row blocks, W_down in registers); DPF == 0: streaming (RB row blocks).
+// Its own function so that each form is compiled on its own: the deduplicating
+// kernel, which picks the form on the device, calls both (one call runs).
+// ---------------------------------------------------------------------------
+template <bool BF16, int MODE, int NT, int RB, bool KF, int DPF, int LAY, bool SH, typename Resolve>
+__device__ __forceinline__ void down_work(const Args& a, Smem<NT * RB>& sm, int& s_last, int item, int units, int T2,
+                                          int ks, Resolve&& resolve) {
+    using F = Fmt<BF16>;
+    constexpr bool PK = LAY == kLayPacked, TL = LAY == kLayTiled;
+    constexpr int P = (2 * RB + NT) <= 3 ? 8 : ((2 * RB + NT) <= 6 ? 4 : 2);  // ring depth, as in the kernel
+    constexpr int H = P / 2;
+    constexpr int RBR = DPF == 2 ? 2 : 1, RBS = RB;  // row blocks: register mode, streaming
+    constexpr int RBM = RBR > RBS ? RBR : RBS;
+    constexpr int PF = DPF == 2 ? kPF / 2 : kPF;     // register mode: W_down steps a wave holds
+    constexpr int RT2 = kTile * (DPF > 0 ? RBR : RBS);  // output rows of a down item
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, q = lane >> 4;
+    const int nm = a.n * a.m;
+    if (item >= units * T2 * ks) return;  // deduplicating kernel: a work group with no role
+    const int ut = item / ks, kp = item - ut * ks;  // contraction part kp of (unit, row tile)
+    const int u = ut / T2, t = ut - u * T2;
+    int32_t* hcnt = a.sync + kLine * u;      // this unit's h-ready count
+    int32_t* dcnt = hcnt + 1;                // this unit's finished down items
+    int32_t* ocnt = a.sync + kLine * (MOE_MAX_SLOTS + t);  // arrivals on this down tile
+    int e, g;
+    bool sh;
+    resolve(u, e, g, sh);
+    // the slots' routing weights and id validity for the combine, loaded now (their
+    // latency hidden behind this item's work; read after the barrier that follows
+    // the arrival) so that a combining work group issues its O loads at once
+    if (tid < nm) {
+        const int id = a.ids[tid];
+        sm.cok[tid] = (id >= 0 && id < a.N) ? 1 : 0;
+        sm.cw[tid] = a.w[tid];
+    }
+    // ================ down: O for RT2 rows of d ================
+    if (g > 0) {
+        const uint32_t mat = (uint32_t)a.d * a.d_ff * F::kEsize;
+        const auto rd = rsrc((SH && sh ? a.wds : a.wd) + (size_t)e * mat, mat);
+        const int nslot = SH ? a.nslot : nm;
+        const uint32_t hbytes = (uint32_t)nslot * a.d_ff * F::kEsize;
+        const auto rh = rsrc(a.h, hbytes);
+        const auto rl = rsrc(a.h + (BF16 ? hbytes : 0), hbytes);
+        const auto ro = rsrc(a.O, (uint32_t)nslot * ks * a.d * 4);
+        // steps kb .. ke-1 of the d_ff contraction (all of it when ks == 1), split
+        // over the four waves: contiguous quarters, or with tiled weights every
+        // fourth step from kb + wave
+        const int S = (a.d_ff + F::kStep - 1) / F::kStep;
+        const int kb = kp * S / ks, kl = (kp + 1) * S / ks - kb;
+        const int s0 = TL ? kb + wave : kb + wave * kl / kWaves;
+        const Steps<BF16, KF, TL ? kWaves : 1> st{
+            s0, TL ? interleaved_steps(kl, wave) : kb + (wave + 1) * kl / kWaves - s0, a.d_ff, q};
+        const PSteps<BF16, KF> pst{s0, st.ns, a.d_ff, a.d, q};  // W_down packed (PK)
+        const TSteps tst{s0, st.ns};                           // W_down tiled (TL)
+        const int ns = st.ns;
+        uint32_t lrow[RBM];
+#pragma unroll
+        for (int rb = 0; rb < RBM; ++rb) {
+            const int row = t * RT2 + rb * kTile + lr;
+            const int r16 = t * RT2 / kTile + rb;  // tiled: row block (d a multiple of 16)
+            lrow[rb] = TL   ? TSteps::lane_base(r16 * kTile < a.d, r16, S, lane)
+                       : PK ? pst.lane_base(row < a.d, row)
+                            : st.lane_base(row < a.d ? (uint32_t)row * a.d_ff * F::kEsize : kOOB);
+        }
+        // W_down chunk of row block rb at wave step j
+        auto wload = [&](int rb, int j) {
+            return TL   ? bload2<0>(rd, tst.vofs(lrow[rb], j), tst.sofs(j))
+                   : PK ? bload2<0>(rd, pst.vofs(lrow[rb], j), pst.sofs(j))
+                        : bload2<0>(rd, st.vofs(lrow[rb], j), st.sofs(j));
+        };
+        if constexpr (DPF > 0) {
+            // All of this wave's W_down rows go to registers before the wait, so
+            // they stream from HBM while gate/up items still run.  After the
+            // wait, h is staged in LDS `gl` tokens at a time (one cooperative
+            // sc1 load per chunk) and the products run from registers and LDS,
+            // for any group size with one read of the weights.
+            extern __shared__ __align__(16) char hs[];  // [gl][hi row, lo row], padded rows
+            u32x4 pa[PF][RBR];
+#pragma unroll
+            for (int i = 0; i < PF; ++i)
+#pragma unroll
+                for (int rb = 0; rb < RBR; ++rb) pa[i][rb] = wload(rb, i);
+            if (tid == 0 && !wait_count(hcnt, a.T1) && a.info) a.info[2] = MOE_E_HIP;
+            __syncthreads();  // h loads (sc1) below are issued after the count was seen
+            const auto rhl = rsrc(a.h, BF16 ? 2 * hbytes : hbytes);  // hi half, then lo half
+            const int rowb = a.d_ff * F::kEsize + 16;      // padded LDS row
+            const int tokb = BF16 ? 2 * rowb : rowb;
+            const int per_row = a.d_ff * F::kEsize / 16;   // 16-byte chunks of an h row
+            for (int cb = 0; cb < g; cb += a.gl) {
+                const int gc = min(a.gl, g - cb);
+                const int nrows = BF16 ? 2 * gc : gc;
+                // kSL loads per thread in flight, then their LDS writes
+                for (int c0 = 0; c0 < nrows * per_row; c0 += kSL * kThreads) {
+                    u32x4 v[kSL];
+                    int dst[kSL];
+#pragma unroll
+                    for (int j = 0; j < kSL; ++j) {
+                        const int c = c0 + j * kThreads + tid;
+                        uint32_t off = kOOB;
+                        dst[j] = -1;
+                        if (c < nrows * per_row) {
+                            const int r = c / per_row, k16 = c - r * per_row;
+                            const int tok = BF16 ? (r >> 1) : r, half = BF16 ? (r & 1) : 0;
+                            off = (uint32_t)half * hbytes + (uint32_t)sm.grp[cb + tok] * a.d_ff * F::kEsize + k16 * 16;
+                            dst[j] = tok * tokb + half * rowb + k16 * 16;
+                        }
+                        v[j] = bload2<kSc1>(rhl, off, 0);
+                    }
+#pragma unroll
+                    for (int j = 0; j < kSL; ++j)
+                        if (dst[j] >= 0) *reinterpret_cast<u32x4*>(hs + dst[j]) = v[j];
+                }
+                __syncthreads();
+                const bool col_ok = lr < gc;
+                const char* bp = hs + (col_ok ? lr : 0) * tokb;  // this lane's token row
+                f32x4 acc[RBR];
+#pragma unroll
+                for (int rb = 0; rb < RBR; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < PF; ++i) {
+                    if (i < ns) {
+                        const int k = st.step(i) * F::kStep + q * F::kPer;
+                        const bool ok = col_ok && k < a.d_ff;
+                        const u32x4 bhv = ok ? *reinterpret_cast<const u32x4*>(bp + k * F::kEsize) : zero4();
+                        u32x4 blv = zero4();
+                        if (BF16 && ok) blv = *reinterpret_cast<const u32x4*>(bp + rowb + k * F::kEsize);
+#pragma unroll
+                        for (int rb = 0; rb < RBR; ++rb) {
+                            acc[rb] = F::mma(pa[i][rb], bhv, acc[rb]);
+                            if (BF16) acc[rb] = F::mma(pa[i][rb], blv, acc[rb]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int rb = 0; rb < RBR; ++rb) sm.red[wave][0][rb][lane] = acc[rb];
+                __syncthreads();
+                if (wave < RBR) {
+                    const int rb = wave;
+                    f32x4 v = sm.red[0][0][rb][lane];
+#pragma unroll
+                    for (int w = 1; w < kWaves; ++w) v += sm.red[w][0][rb][lane];
+                    const int i0 = t * RT2 + rb * kTile + 4 * q;
+                    if (col_ok && i0 < a.d)  // d % 8 == 0: rows i0..i0+3 all valid
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro,
+                                                               (((uint32_t)sm.grp[cb + lr] * ks + kp) * a.d + i0) * 4, 0,
+                                                               kSc1);
+                    stores_complete();
+                }
+                __syncthreads();
+            }
+        } else
+        for (int base = 0; base < g; base += 16 * NT) {
+            u32x4 ad[P][RBS], bh[P][NT], bl[P][NT];
+            uint32_t lh[NT];
+            auto issue_a = [&](int slot, int j) {
+#pragma unroll
+                for (int rb = 0; rb < RBS; ++rb) ad[slot][rb] = wload(rb, j);
+            };
+            auto issue_b = [&](int slot, int j) {
+                const uint32_t so = st.sofs(j);
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) {
+                    bh[slot][tt] = bload2<kSc1>(rh, st.vofs(lh[tt], j), so);
+                    if (BF16) bl[slot][tt] = bload2<kSc1>(rl, st.vofs(lh[tt], j), so);
+                }
+            };
+#pragma unroll
+            for (int i = 0; i < P; ++i) {  // weights first, in slot order (see gate_up)
+                issue_a(i, i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (base == 0) {
+                if (tid == 0 && !wait_count(hcnt, a.T1) && a.info) a.info[2] = MOE_E_HIP;
+                __syncthreads();  // h loads (sc1) below are issued after the count was seen
+            }
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const int gi = base + tt * 16 + lr;
+                lh[tt] = st.lane_base(gi < g ? (uint32_t)sm.grp[gi] * a.d_ff * F::kEsize : kOOB);
+            }
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+                issue_b(i, i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            f32x4 acc[RBS][NT];
+#pragma unroll
+            for (int rb = 0; rb < RBS; ++rb)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) acc[rb][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < ns; s += P) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                    for (int i = hh * H; i < hh * H + H; ++i)
+#pragma unroll
+                        for (int rb = 0; rb < RBS; ++rb)
+#pragma unroll
+                            for (int tt = 0; tt < NT; ++tt) {
+                                acc[rb][tt] = F::mma(ad[i][rb], bh[i][tt], acc[rb][tt]);
+                                if (BF16) acc[rb][tt] = F::mma(ad[i][rb], bl[i][tt], acc[rb][tt]);
+                            }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = hh * H; i < hh * H + H; ++i) {
+                        issue_a(i, s + i + P);
+                        issue_b(i, s + i + P);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+#pragma unroll
+            for (int rb = 0; rb < RBS; ++rb)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) sm.red[wave][0][rb * NT + tt][lane] = acc[rb][tt];
+            __syncthreads();
+            if (wave < RBS * NT) {
+                const int rb = wave / NT, tt = wave - rb * NT;
+                f32x4 v = sm.red[0][0][wave][lane];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w) v += sm.red[w][0][wave][lane];
+                const int gi = base + tt * 16 + lr;
+                const int i0 = t * RT2 + rb * kTile + 4 * q;
+                if (gi < g && i0 < a.d)  // d % 8 == 0: rows i0..i0+3 all valid
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro,
+                                                           (((uint32_t)sm.grp[gi] * ks + kp) * a.d + i0) * 4, 0, kSc1);
+                stores_complete();
+            }
+            __syncthreads();
+        }
+        // the unit's last down item resets the unit's counters for the next call
+        // (every down item of the unit has seen the full h-ready count by now)
+        if (tid == 0 && atomicAdd(dcnt, 1) == T2 * ks - 1) {
+            __hip_atomic_store(hcnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(dcnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    // arrival on this row tile; the last unit to arrive combines its rows
+    if (tid == 0) {
+        const int old = atomicAdd(ocnt, 1);  // after the writers' completed stores and the barrier
+        s_last = old == units * ks - 1;
+        if (s_last) __hip_atomic_store(ocnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // all arrived
+    }
+    __syncthreads();  // O loads (sc1) below are issued after the last arrival was seen
+    if (s_last) {
+        // y_t = sum_j w_tj sum_p O_(tj, p) + sum_s sum_p O_(shared s, t, p) for 4 rows
+        // per thread: slots in increasing j, then shared experts in increasing s,
+        // each slot's contraction parts p in increasing order (w_tj applied to each
+        // part); the O loads (sc1) of up to kCJ (slot, part) pairs are in flight
+        // together
+        constexpr int kCJ = 8;
+        const int i0 = t * RT2;
+        const int q4 = min(RT2, a.d - i0) / 4;  // d % 8 == 0
+        const auto rO = rsrc(a.O, (uint32_t)(SH ? a.nslot : nm) * ks * a.d * 4);
+        const int nr = a.m * ks;                                  // routed (slot, part) pairs of a token
+        const int npair = nr + (SH ? a.n_shared * ks : 0);        // and the shared experts' pairs
+        for (int o = tid; o < a.n * q4; o += kThreads) {
+            const int tok = o / q4, i = i0 + 4 * (o - tok * q4);
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int c0 = 0; c0 < npair; c0 += kCJ) {
+                u32x4 ov[kCJ];
+                float wv[kCJ];
+                bool ok[kCJ];
+#pragma unroll
+                for (int jj = 0; jj < kCJ; ++jj) {
+                    const int c = c0 + jj;
+                    int sl = -1;
+                    float wgt = 1.f;
+                    if (c < nr) {
+                        const int s = tok * a.m + c / ks;
+                        if (sm.cok[s]) {
+                            sl = s;
+                            wgt = sm.cw[s];
+                        }
+                    } else if (SH && c < npair) {
+                        sl = nm + ((c - nr) / ks) * a.n + tok;
+                    }
+                    ok[jj] = sl >= 0;
+                    wv[jj] = wgt;
+                    ov[jj] = bload_sc1(rO, ok[jj] ? (((uint32_t)sl * ks + c % ks) * a.d + i) * 4 : kOOB);
+                }
+#pragma unroll
+                for (int jj = 0; jj < kCJ; ++jj)
+                    if (ok[jj])
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[r] = fmaf(wv[jj], __uint_as_float(ov[jj][r]), acc[r]);
+            }
+            f32x4* yp = reinterpret_cast<f32x4*>(a.y + (size_t)tok * a.d + i);
+            if (a.accumulate) acc += *yp;  // y is read only when the call accumulates
+            *yp = acc;
+        }
+    }
+}
+
 // The per-slot kernel with down items in registers and one token tile holds its
 // registers to 4 waves per SIMD, so that a small pass's gate/up and down work
 // groups are all resident at once (a performance choice: every wait is on a lower
@@ -614,22 +931,16 @@ constexpr int kSL = 4;  // register mode: h staging loads in flight per thread
 template <bool BF16, int MODE, int NT, int RB, bool KF, int DPF, int LAY, bool SH>
 __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) ? 4 : (NT == 2 ? 3 : 1)) void k_expert(
     Args a) {
-    using F = Fmt<BF16>;
-    constexpr bool PK = LAY == kLayPacked, TL = LAY == kLayTiled;
+    constexpr bool TL = LAY == kLayTiled;
     // ring depth in steps: operand registers per step are (2*RB + NT) for gate/up
     // and (RB + 2*NT) for down, 4 VGPRs each
     constexpr int P = (2 * RB + NT) <= 3 ? 8 : ((2 * RB + NT) <= 6 ? 4 : 2);
-    constexpr int H = P / 2;  // half ring
-    // down items: one row block in register mode (the W_down rows a wave holds),
-    // else RB like the gate/up items
-    constexpr int RB2 = DPF == 2 ? 2 : (DPF == 1 ? 1 : RB);
-    constexpr int PF = DPF == 2 ? kPF / 2 : kPF;  // register mode: W_down steps a wave holds
-    constexpr int RT2 = kTile * RB2;
+    // down items: row blocks in register mode (RBR: the W_down rows a wave holds),
+    // streaming RB like the gate/up items (down_work)
+    constexpr int RBR = DPF == 2 ? 2 : 1, RBS = RB;
     __shared__ Smem<NT * RB> sm;
     __shared__ int s_last;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so step offsets are scalar
-    const int lr = lane & 15, q = lane >> 4;
+    const int tid = threadIdx.x;
     const int nm = a.n * a.m;
     const bool want_status = a.info != nullptr && blockIdx.x == 0;
 
@@ -660,6 +971,19 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) 
         }
     }
     const bool phase1 = (int)blockIdx.x < g1;
+    // Down items in register mode or streaming (down_shape).  The per-slot kernel's
+    // shape is the host's; the deduplicating kernel takes it for its real units (its
+    // variants with DPF > 0 are those where the host found a wave's share of W_down
+    // and the largest group's h fit, so register mode is allowed), streaming with
+    // the host's contraction parts a.ks.
+    bool reg = DPF > 0;
+    int T2 = a.T2, ks = a.ks;
+    if (MODE == kDedup) {
+        const DownShape ds = down_shape(units, g1, a.d, DPF > 0, RBR, RBS, a.reg_wgs, a.ks);
+        reg = DPF > 0 && ds.reg;
+        T2 = ds.T2;
+        ks = ds.ks;
+    }
 
     // The unit u: expert e and its slots sm.grp[0..g); sh: e is a shared expert (all
     // n tokens, weight 1, slots nm + e*n + t).
@@ -726,281 +1050,10 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) 
         }
     } else {
         const int item = (int)blockIdx.x - g1;
-        if (item >= units * a.T2 * a.ks) return;  // deduplicating kernel: a work group with no role
-        const int ut = item / a.ks, kp = item - ut * a.ks;  // contraction part kp of (unit, row tile)
-        const int u = ut / a.T2, t = ut - u * a.T2;
-        int32_t* hcnt = a.sync + kLine * u;      // this unit's h-ready count
-        int32_t* dcnt = hcnt + 1;                // this unit's finished down items
-        int32_t* ocnt = a.sync + kLine * (MOE_MAX_SLOTS + t);  // arrivals on this down tile
-        int e, g;
-        bool sh;
-        resolve(u, e, g, sh);
-        // the slots' routing weights and id validity for the combine, loaded now (their
-        // latency hidden behind this item's work; read after the barrier that follows
-        // the arrival) so that a combining work group issues its O loads at once
-        if (tid < nm) {
-            const int id = a.ids[tid];
-            sm.cok[tid] = (id >= 0 && id < a.N) ? 1 : 0;
-            sm.cw[tid] = a.w[tid];
-        }
-        // ================ down: O for RT2 rows of d ================
-        if (g > 0) {
-            const uint32_t mat = (uint32_t)a.d * a.d_ff * F::kEsize;
-            const auto rd = rsrc((SH && sh ? a.wds : a.wd) + (size_t)e * mat, mat);
-            const int nslot = SH ? a.nslot : nm;
-            const uint32_t hbytes = (uint32_t)nslot * a.d_ff * F::kEsize;
-            const auto rh = rsrc(a.h, hbytes);
-            const auto rl = rsrc(a.h + (BF16 ? hbytes : 0), hbytes);
-            const auto ro = rsrc(a.O, (uint32_t)nslot * a.ks * a.d * 4);
-            // steps kb .. ke-1 of the d_ff contraction (all of it when ks == 1), split
-            // over the four waves: contiguous quarters, or with tiled weights every
-            // fourth step from kb + wave
-            const int S = (a.d_ff + F::kStep - 1) / F::kStep;
-            const int kb = kp * S / a.ks, kl = (kp + 1) * S / a.ks - kb;
-            const int s0 = TL ? kb + wave : kb + wave * kl / kWaves;
-            const Steps<BF16, KF, TL ? kWaves : 1> st{
-                s0, TL ? interleaved_steps(kl, wave) : kb + (wave + 1) * kl / kWaves - s0, a.d_ff, q};
-            const PSteps<BF16, KF> pst{s0, st.ns, a.d_ff, a.d, q};  // W_down packed (PK)
-            const TSteps tst{s0, st.ns};                           // W_down tiled (TL)
-            const int ns = st.ns;
-            uint32_t lrow[RB2];
-#pragma unroll
-            for (int rb = 0; rb < RB2; ++rb) {
-                const int row = t * RT2 + rb * kTile + lr;
-                const int r16 = t * RB2 + rb;  // tiled: row block (d a multiple of 16)
-                lrow[rb] = TL   ? TSteps::lane_base(r16 * kTile < a.d, r16, S, lane)
-                           : PK ? pst.lane_base(row < a.d, row)
-                                : st.lane_base(row < a.d ? (uint32_t)row * a.d_ff * F::kEsize : kOOB);
-            }
-            // W_down chunk of row block rb at wave step j
-            auto wload = [&](int rb, int j) {
-                return TL   ? bload2<0>(rd, tst.vofs(lrow[rb], j), tst.sofs(j))
-                       : PK ? bload2<0>(rd, pst.vofs(lrow[rb], j), pst.sofs(j))
-                            : bload2<0>(rd, st.vofs(lrow[rb], j), st.sofs(j));
-            };
-            if constexpr (DPF > 0) {
-                // All of this wave's W_down rows go to registers before the wait, so
-                // they stream from HBM while gate/up items still run.  After the
-                // wait, h is staged in LDS `gl` tokens at a time (one cooperative
-                // sc1 load per chunk) and the products run from registers and LDS,
-                // for any group size with one read of the weights.
-                extern __shared__ __align__(16) char hs[];  // [gl][hi row, lo row], padded rows
-                u32x4 pa[PF][RB2];
-#pragma unroll
-                for (int i = 0; i < PF; ++i)
-#pragma unroll
-                    for (int rb = 0; rb < RB2; ++rb) pa[i][rb] = wload(rb, i);
-                if (tid == 0 && !wait_count(hcnt, a.T1) && a.info) a.info[2] = MOE_E_HIP;
-                __syncthreads();  // h loads (sc1) below are issued after the count was seen
-                const auto rhl = rsrc(a.h, BF16 ? 2 * hbytes : hbytes);  // hi half, then lo half
-                const int rowb = a.d_ff * F::kEsize + 16;      // padded LDS row
-                const int tokb = BF16 ? 2 * rowb : rowb;
-                const int per_row = a.d_ff * F::kEsize / 16;   // 16-byte chunks of an h row
-                for (int cb = 0; cb < g; cb += a.gl) {
-                    const int gc = min(a.gl, g - cb);
-                    const int nrows = BF16 ? 2 * gc : gc;
-                    // kSL loads per thread in flight, then their LDS writes
-                    for (int c0 = 0; c0 < nrows * per_row; c0 += kSL * kThreads) {
-                        u32x4 v[kSL];
-                        int dst[kSL];
-#pragma unroll
-                        for (int j = 0; j < kSL; ++j) {
-                            const int c = c0 + j * kThreads + tid;
-                            uint32_t off = kOOB;
-                            dst[j] = -1;
-                            if (c < nrows * per_row) {
-                                const int r = c / per_row, k16 = c - r * per_row;
-                                const int tok = BF16 ? (r >> 1) : r, half = BF16 ? (r & 1) : 0;
-                                off = (uint32_t)half * hbytes + (uint32_t)sm.grp[cb + tok] * a.d_ff * F::kEsize + k16 * 16;
-                                dst[j] = tok * tokb + half * rowb + k16 * 16;
-                            }
-                            v[j] = bload2<kSc1>(rhl, off, 0);
-                        }
-#pragma unroll
-                        for (int j = 0; j < kSL; ++j)
-                            if (dst[j] >= 0) *reinterpret_cast<u32x4*>(hs + dst[j]) = v[j];
-                    }
-                    __syncthreads();
-                    const bool col_ok = lr < gc;
-                    const char* bp = hs + (col_ok ? lr : 0) * tokb;  // this lane's token row
-                    f32x4 acc[RB2];
-#pragma unroll
-                    for (int rb = 0; rb < RB2; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int i = 0; i < PF; ++i) {
-                        if (i < ns) {
-                            const int k = st.step(i) * F::kStep + q * F::kPer;
-                            const bool ok = col_ok && k < a.d_ff;
-                            const u32x4 bhv = ok ? *reinterpret_cast<const u32x4*>(bp + k * F::kEsize) : zero4();
-                            u32x4 blv = zero4();
-                            if (BF16 && ok) blv = *reinterpret_cast<const u32x4*>(bp + rowb + k * F::kEsize);
-#pragma unroll
-                            for (int rb = 0; rb < RB2; ++rb) {
-                                acc[rb] = F::mma(pa[i][rb], bhv, acc[rb]);
-                                if (BF16) acc[rb] = F::mma(pa[i][rb], blv, acc[rb]);
-                            }
-                        }
-                    }
-#pragma unroll
-                    for (int rb = 0; rb < RB2; ++rb) sm.red[wave][0][rb][lane] = acc[rb];
-                    __syncthreads();
-                    if (wave < RB2) {
-                        const int rb = wave;
-                        f32x4 v = sm.red[0][0][rb][lane];
-#pragma unroll
-                        for (int w = 1; w < kWaves; ++w) v += sm.red[w][0][rb][lane];
-                        const int i0 = t * RT2 + rb * kTile + 4 * q;
-                        if (col_ok && i0 < a.d)  // d % 8 == 0: rows i0..i0+3 all valid
-                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro,
-                                                                   (((uint32_t)sm.grp[cb + lr] * a.ks + kp) * a.d + i0) * 4, 0,
-                                                                   kSc1);
-                        stores_complete();
-                    }
-                    __syncthreads();
-                }
-            } else
-            for (int base = 0; base < g; base += 16 * NT) {
-                u32x4 ad[P][RB2], bh[P][NT], bl[P][NT];
-                uint32_t lh[NT];
-                auto issue_a = [&](int slot, int j) {
-#pragma unroll
-                    for (int rb = 0; rb < RB2; ++rb) ad[slot][rb] = wload(rb, j);
-                };
-                auto issue_b = [&](int slot, int j) {
-                    const uint32_t so = st.sofs(j);
-#pragma unroll
-                    for (int tt = 0; tt < NT; ++tt) {
-                        bh[slot][tt] = bload2<kSc1>(rh, st.vofs(lh[tt], j), so);
-                        if (BF16) bl[slot][tt] = bload2<kSc1>(rl, st.vofs(lh[tt], j), so);
-                    }
-                };
-#pragma unroll
-                for (int i = 0; i < P; ++i) {  // weights first, in slot order (see gate_up)
-                    issue_a(i, i);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                if (base == 0) {
-                    if (tid == 0 && !wait_count(hcnt, a.T1) && a.info) a.info[2] = MOE_E_HIP;
-                    __syncthreads();  // h loads (sc1) below are issued after the count was seen
-                }
-#pragma unroll
-                for (int tt = 0; tt < NT; ++tt) {
-                    const int gi = base + tt * 16 + lr;
-                    lh[tt] = st.lane_base(gi < g ? (uint32_t)sm.grp[gi] * a.d_ff * F::kEsize : kOOB);
-                }
-#pragma unroll
-                for (int i = 0; i < P; ++i) {
-                    issue_b(i, i);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                f32x4 acc[RB2][NT];
-#pragma unroll
-                for (int rb = 0; rb < RB2; ++rb)
-#pragma unroll
-                    for (int tt = 0; tt < NT; ++tt) acc[rb][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                for (int s = 0; s < ns; s += P) {
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-                        for (int i = hh * H; i < hh * H + H; ++i)
-#pragma unroll
-                            for (int rb = 0; rb < RB2; ++rb)
-#pragma unroll
-                                for (int tt = 0; tt < NT; ++tt) {
-                                    acc[rb][tt] = F::mma(ad[i][rb], bh[i][tt], acc[rb][tt]);
-                                    if (BF16) acc[rb][tt] = F::mma(ad[i][rb], bl[i][tt], acc[rb][tt]);
-                                }
-                        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                        for (int i = hh * H; i < hh * H + H; ++i) {
-                            issue_a(i, s + i + P);
-                            issue_b(i, s + i + P);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-#pragma unroll
-                for (int rb = 0; rb < RB2; ++rb)
-#pragma unroll
-                    for (int tt = 0; tt < NT; ++tt) sm.red[wave][0][rb * NT + tt][lane] = acc[rb][tt];
-                __syncthreads();
-                if (wave < RB2 * NT) {
-                    const int rb = wave / NT, tt = wave - rb * NT;
-                    f32x4 v = sm.red[0][0][wave][lane];
-#pragma unroll
-                    for (int w = 1; w < kWaves; ++w) v += sm.red[w][0][wave][lane];
-                    const int gi = base + tt * 16 + lr;
-                    const int i0 = t * RT2 + rb * kTile + 4 * q;
-                    if (gi < g && i0 < a.d)  // d % 8 == 0: rows i0..i0+3 all valid
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro,
-                                                               (((uint32_t)sm.grp[gi] * a.ks + kp) * a.d + i0) * 4, 0, kSc1);
-                    stores_complete();
-                }
-                __syncthreads();
-            }
-            // the unit's last down item resets the unit's counters for the next call
-            // (every down item of the unit has seen the full h-ready count by now)
-            if (tid == 0 && atomicAdd(dcnt, 1) == a.T2 * a.ks - 1) {
-                __hip_atomic_store(hcnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(dcnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        // arrival on this row tile; the last unit to arrive combines its rows
-        if (tid == 0) {
-            const int old = atomicAdd(ocnt, 1);  // after the writers' completed stores and the barrier
-            s_last = old == units * a.ks - 1;
-            if (s_last) __hip_atomic_store(ocnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // all arrived
-        }
-        __syncthreads();  // O loads (sc1) below are issued after the last arrival was seen
-        if (s_last) {
-            // y_t = sum_j w_tj sum_p O_(tj, p) + sum_s sum_p O_(shared s, t, p) for 4 rows
-            // per thread: slots in increasing j, then shared experts in increasing s,
-            // each slot's contraction parts p in increasing order (w_tj applied to each
-            // part); the O loads (sc1) of up to kCJ (slot, part) pairs are in flight
-            // together
-            constexpr int kCJ = 8;
-            const int ks = a.ks;
-            const int i0 = t * RT2;
-            const int q4 = min(RT2, a.d - i0) / 4;  // d % 8 == 0
-            const auto rO = rsrc(a.O, (uint32_t)(SH ? a.nslot : nm) * ks * a.d * 4);
-            const int nr = a.m * ks;                                  // routed (slot, part) pairs of a token
-            const int npair = nr + (SH ? a.n_shared * ks : 0);        // and the shared experts' pairs
-            for (int o = tid; o < a.n * q4; o += kThreads) {
-                const int tok = o / q4, i = i0 + 4 * (o - tok * q4);
-                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-                for (int c0 = 0; c0 < npair; c0 += kCJ) {
-                    u32x4 ov[kCJ];
-                    float wv[kCJ];
-                    bool ok[kCJ];
-#pragma unroll
-                    for (int jj = 0; jj < kCJ; ++jj) {
-                        const int c = c0 + jj;
-                        int sl = -1;
-                        float wgt = 1.f;
-                        if (c < nr) {
-                            const int s = tok * a.m + c / ks;
-                            if (sm.cok[s]) {
-                                sl = s;
-                                wgt = sm.cw[s];
-                            }
-                        } else if (SH && c < npair) {
-                            sl = nm + ((c - nr) / ks) * a.n + tok;
-                        }
-                        ok[jj] = sl >= 0;
-                        wv[jj] = wgt;
-                        ov[jj] = bload_sc1(rO, ok[jj] ? (((uint32_t)sl * ks + c % ks) * a.d + i) * 4 : kOOB);
-                    }
-#pragma unroll
-                    for (int jj = 0; jj < kCJ; ++jj)
-                        if (ok[jj])
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) acc[r] = fmaf(wv[jj], __uint_as_float(ov[jj][r]), acc[r]);
-                }
-                f32x4* yp = reinterpret_cast<f32x4*>(a.y + (size_t)tok * a.d + i);
-                if (a.accumulate) acc += *yp;  // y is read only when the call accumulates
-                *yp = acc;
-            }
-        }
+        if (MODE == kDedup && DPF > 0 && !reg)
+            down_work<BF16, MODE, NT, RB, KF, 0, LAY, SH>(a, sm, s_last, item, units, T2, ks, resolve);
+        else
+            down_work<BF16, MODE, NT, RB, KF, DPF, LAY, SH>(a, sm, s_last, item, units, T2, ks, resolve);
     }
 }
 
@@ -1009,7 +1062,11 @@ struct Plan {
     int g1, S1;  // gate/up work groups, K steps per gate/up tile
     bool split_ok;  // the workspace holds partial sums of split gate/up tiles
     size_t part_off;
-    int dpf;     // down items: 0 streaming, 1 register mode (16 rows), 2 register mode (32 rows)
+    int dpf;     // down items: 0 streaming, 1 register mode (16 rows), 2 register mode (32 rows);
+                 // deduplicating kernel: register mode allowed, decided on the device
+    int reg_wgs; // most work groups of a pass with register-mode down items
+    int down_wgs;  // down work groups of the grid
+    int grid;      // work groups of the launch
     int gl;      // register mode: tokens of h staged in LDS at a time
     size_t lds;  // register mode: dynamic LDS bytes
     size_t h_off, o_off, sync_off, total;

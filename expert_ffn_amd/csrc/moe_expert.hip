@@ -360,7 +360,6 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int kMaxKs = 4;  // contraction parts of a streaming down item
 
 int check_desc(const moe_layer_desc* d, int32_t n) {
     if (!d) return MOE_E_INVAL;
@@ -392,7 +391,7 @@ int check_desc(const moe_layer_desc* d, int32_t n) {
 // work groups per compute unit at once: the per-slot register-mode kernel's launch
 // bound, and what the deduplicating kernel's registers allow
 constexpr int kResidentSlot = 4, kResidentDedup = 3;
-constexpr int kHsBudget = 24 * 1024;  // LDS bytes for staged h (down items in register mode)
+constexpr int kHsBudget = 32 * 1024;  // LDS bytes for staged h (down items in register mode)
 // per-slot passes with shared experts: LDS for the shared experts' h chunks
 constexpr int kHsBudgetShared = 12 * 1024;
 
@@ -440,7 +439,10 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     // resident during gate/up; items dispatched after it run in rounds of short,
     // latency-bound work, where streaming items (twice the rows, a load ring) do
     // better.  Same-box: every pass measured at 2.7 rounds or fewer was faster in
-    // register mode, every one at 3 or more faster streaming.
+    // register mode, every one at 3 or more faster streaming.  The deduplicating
+    // kernel counts its rounds on the device, over its real units (the U distinct
+    // experts are not known here): its launch carries both forms of down item and the
+    // grid covers the larger.
     const int s2 = (d->d_ff + step - 1) / step;
     const int per_tok = (d->d_ff * es + 16) * (bf ? 2 : 1);  // staged bytes per token
     const int gmax = kind == MOE_KIND_SLOT ? 1 : n;  // routed group size is at most n (valid ids)
@@ -448,25 +450,53 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     const int wsteps = (s2 + kWaves - 1) / kWaves;  // a wave's share of the down contraction
     const bool kf = d->d_model % step == 0 && d->d_ff % step == 0;
     const int reg_rows = (kf && wsteps <= kPF / 2) ? 2 : 1;  // row blocks of a register-mode item
-    const int64_t dpf_items = (int64_t)p.units * ((d->d_model + kTile * reg_rows - 1) / (kTile * reg_rows));
-    const bool reg_ok = wsteps <= kPF && 4 * (p.g1 + dpf_items) <= 11 * resident;
+    p.reg_wgs = (int)(11 * resident / 4);  // (resident is a multiple of 4)
+    bool reg_allowed;
     if (kind == MOE_KIND_SLOT && d->n_shared > 0) {
         const int cap = (int)std::max<int64_t>(1, kHsBudgetShared / per_tok);
-        p.dpf = (reg_ok && (int64_t)per_tok <= kHsBudget) ? reg_rows : 0;
-        p.gl = p.dpf ? std::min(n, std::min(cap, 16)) : 0;
+        reg_allowed = wsteps <= kPF && (int64_t)per_tok <= kHsBudget;
+        p.gl = reg_allowed ? std::min(n, std::min(cap, 16)) : 0;
     } else {
-        p.dpf = (reg_ok && gmax <= 16 && (int64_t)per_tok * gmax <= kHsBudget) ? reg_rows : 0;
-        p.gl = p.dpf ? gmax : 0;
+        reg_allowed = wsteps <= kPF && gmax <= 16 && (int64_t)per_tok * gmax <= kHsBudget;
+        p.gl = reg_allowed ? gmax : 0;
     }
-    p.lds = p.dpf ? (size_t)p.gl * per_tok : 0;
-    const int rb2 = p.dpf ? p.dpf : p.rb;
-    p.T2 = (d->d_model + kTile * rb2 - 1) / (kTile * rb2);
     // Streaming down items (not register mode) each stream their rows' W_down after
     // the wait, at what one work group keeps in flight; with fewer than 4 items per
     // compute unit the d_ff contraction of each (unit, row tile) is cut into ks
-    // parts, one item each, summed in the combine.
-    const int64_t ditems = (int64_t)p.units * p.T2;
-    p.ks = p.dpf ? 1 : (int)std::min<int64_t>(kMaxKs, std::max<int64_t>(1, (4 * kCUs + ditems - 1) / ditems));
+    // parts, one item each, summed in the combine.  For the deduplicating kernel the
+    // parts are counted over the planned units, min(n m, N) routed: counted over its
+    // real units instead (more parts when fewer experts are distinct), the same-box
+    // bench was 7 us slower on the DeepSeek-V2-Lite shape at n = 4 (correlated),
+    // 5-7 us on the Mixtral shape at n = 4..8 (uniform), 6 us faster only on the
+    // Mixtral shape at n = 2 (correlated).
+    const int t2s = (d->d_model + kTile * p.rb - 1) / (kTile * p.rb);
+    const int64_t ditems = (int64_t)p.units * t2s;
+    const int ks_s = (int)std::min<int64_t>(kMaxKs, std::max<int64_t>(1, (4 * kCUs + ditems - 1) / ditems));
+    const DownShape ds = down_shape(p.units, p.g1, d->d_model, reg_allowed, reg_rows, p.rb, p.reg_wgs, ks_s);
+    p.T2 = ds.T2;
+    p.ks = ds.ks;
+    if (kind == MOE_KIND_SLOT) {
+        p.dpf = ds.reg ? reg_rows : 0;
+        p.down_wgs = p.units * p.T2 * p.ks;
+        p.grid = p.g1 + p.down_wgs;
+    } else {
+        // the device takes the shape for the U distinct experts it finds; the grid
+        // covers the largest pass, gate/up and down work groups, over every U
+        p.dpf = reg_allowed ? reg_rows : 0;
+        p.grid = 0;
+        bool streams = false;
+        for (int U = 1; U <= p.units_r; ++U) {
+            const int units = U + d->n_shared;
+            const int g1 = gate_up_groups(units * p.T1, p.S1, p.split_ok, kDedupSplitUpper);
+            const DownShape du = down_shape(units, g1, d->d_model, reg_allowed, reg_rows, p.rb, p.reg_wgs, ks_s);
+            p.grid = std::max(p.grid, g1 + units * du.T2 * du.ks);
+            streams |= !du.reg;
+        }
+        p.down_wgs = p.grid - p.g1;
+        p.ks = streams ? ks_s : 1;  // O holds the streaming form's parts if it may stream
+    }
+    if (!p.dpf) p.gl = 0;
+    p.lds = p.dpf ? (size_t)p.gl * per_tok : 0;
     p.sync_off = 0;
     p.h_off = (size_t)kSyncWords * 4;
     p.o_off = p.h_off + align_up((size_t)p.nslot * d->d_ff * 4);
@@ -535,8 +565,9 @@ int run_expert(const moe_layer_desc* d, const moe_layer_weights* W, const void* 
     args.g1 = p.g1;
     args.S1 = p.S1;
     args.split_ok = p.split_ok ? 1 : 0;
+    args.reg_wgs = p.reg_wgs;
     args.part = reinterpret_cast<float*>(wsb + p.part_off);
-    const int grid = p.g1 + p.units * p.T2 * p.ks;
+    const int grid = p.grid;
     (void)hipGetLastError();
     if (clear_counters)  // a workspace whose counters may not be zero (a shared array): clear them first
         hipLaunchKernelGGL(k_zero_words, dim3((kSyncWords + 255) / 256), dim3(256), 0, st,

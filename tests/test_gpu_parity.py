@@ -264,6 +264,24 @@ def test_dsv2lite_windows(dsv2_by_layout, kind, layout):
         _compare(dsv2, x, ids, w, "dsv2lite %s n=%d" % (kind, n), shared=sh)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_dedup_down_form_follows_distinct_experts(dsv2_by_layout, layout):
+    """The deduplicating kernel picks register-mode or streaming down items on the
+    device, from the U distinct experts it finds.  DeepSeek-V2-Lite shape, both shared
+    experts in the call, n = 2, passes naming exactly U = 6 .. 12 experts: with
+    U + 2 units of 44 gate/up tiles and 128 register-mode items each, the pass fits
+    the 2112 work groups of register mode up to U = 10 (528 + 1536) and streams from
+    U = 11 (572 + 1664); every pass matches the oracle and the per-slot kernel."""
+    dsv2 = dsv2_by_layout[layout]
+    spec = dsv2.spec
+    rng = np.random.default_rng(77)
+    x = synth.pass_x(spec, 2026, 0, 2000, 2)
+    for U in range(6, 13):
+        ids, w = routing.chosen_pass(spec.N, spec.m, 2, U, rng)
+        say("dsv2lite chosen U", U, layout)
+        _compare(dsv2, x, ids, w, "dsv2lite n=2 U=%d" % U, shared="fused")
+
+
 @pytest.mark.parametrize("base,n_shared,d,d_ff", [("tiny", 1, 64, 128), ("tiny", 3, 72, 40),
                                                    ("dsv2lite", 2, 96, 160), ("dsv2lite", 1, 256, 352)])
 @pytest.mark.parametrize("layout", LAYOUTS)
