@@ -383,10 +383,13 @@ __host__ __device__ inline int gate_up_groups(int tiles, int S1, bool split_ok, 
 
 // Down items of a pass of `units` units whose gate/up work takes g1 work groups: in
 // register mode (rbr row blocks an item, the whole d_ff contraction) when it is
-// allowed and the pass's work groups, the g1 and these items, number at most
-// reg_wgs (about 11/4 rounds of what the compute units hold at once); else
-// streaming (rbs row blocks an item), the d_ff contraction of each (unit, row tile)
-// cut into ks_s parts.
+// allowed and either its items hold 32 rows (rbr = 2, as many rows as a streaming
+// item) or the pass's work groups, the g1 and these items, number at most reg_wgs
+// (about 11/4 rounds of what the compute units hold at once); else streaming (rbs
+// row blocks an item), the d_ff contraction of each (unit, row tile) cut into ks_s
+// parts.  Register-mode items of 16 rows measured slower than streaming items of
+// 32 from 3 rounds on; those of 32 rows were faster at every round count measured
+// (Qwen3 shape per-slot, 3.4 to 5.5 rounds at n = 5..8: 5-6 % per pass).
 constexpr int kMaxKs = 4;  // contraction parts of a streaming down item, at most
 struct DownShape {
     int reg, T2, ks;
@@ -394,7 +397,7 @@ struct DownShape {
 __host__ __device__ inline DownShape down_shape(int units, int g1, int d, bool reg_allowed, int rbr, int rbs,
                                                 int reg_wgs, int ks_s) {
     const int t2r = (d + kTile * rbr - 1) / (kTile * rbr);
-    if (reg_allowed && g1 + units * t2r <= reg_wgs) return DownShape{1, t2r, 1};
+    if (reg_allowed && (rbr == 2 || g1 + units * t2r <= reg_wgs)) return DownShape{1, t2r, 1};
     return DownShape{0, (d + kTile * rbs - 1) / (kTile * rbs), ks_s};
 }
 

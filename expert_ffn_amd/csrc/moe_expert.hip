@@ -439,7 +439,9 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     // resident during gate/up; items dispatched after it run in rounds of short,
     // latency-bound work, where streaming items (twice the rows, a load ring) do
     // better.  Same-box: every pass measured at 2.7 rounds or fewer was faster in
-    // register mode, every one at 3 or more faster streaming.  The deduplicating
+    // register mode, every one at 3 or more faster streaming; this holds for
+    // register-mode items of 16 rows, while items of 32 rows (a wave's share at most
+    // kPF / 2 steps) are taken at any round count (down_shape).  The deduplicating
     // kernel counts its rounds on the device, over its real units (the U distinct
     // experts are not known here): its launch carries both forms of down item and the
     // grid covers the larger.
