@@ -1,0 +1,66 @@
+// Host check of the gate/up work split (gate_up_groups in expert_kernel.h) and of
+// the share arithmetic k_expert uses with it: for every plan over a range of tile
+// counts, K step counts and upper bounds, every (tile, K step) is covered by
+// exactly one work group; for every tile, the contributors the kernel computes
+// (first .. last) are exactly the work groups whose shares meet the tile, in K
+// order and consecutive, at most kMaxContrib of them, so the finaliser (the last)
+// holds the highest id; cut tiles' counter indices stay below kMaxSplitTiles; and
+// the arithmetic stays below 2^31.  Prints "ok <plans checked>" or the first failure.
+#include <cstdio>
+#include <vector>
+#include "../../expert_ffn_amd/csrc/expert_kernel.h"
+
+using namespace moe_k;
+
+static int fail(int tiles, int S1, int upper, const char* what) {
+    std::printf("FAIL tiles=%d S1=%d upper=%d: %s\n", tiles, S1, upper, what);
+    return 1;
+}
+
+int main() {
+    long plans = 0;
+    const int uppers[] = {2 * kCUs, kDedupSplitUpper};
+    for (int upper : uppers)
+        for (int S1 : {1, 2, 3, 5, 24, 64, 128, 448, 512})
+            for (int tiles = 1; tiles <= 3 * kCUs + 40; ++tiles) {
+                for (int ok = 0; ok < 2; ++ok) {
+                    const int g1 = gate_up_groups(tiles, S1, ok != 0, upper);
+                    const bool split = g1 != tiles;  // as the kernel: some tile is cut
+                    if (!ok && split) return fail(tiles, S1, upper, "cut without room");
+                    const long ltot = (long)tiles * S1;
+                    if (split && (ltot + S1) * (long)(g1 + 1) >= (1l << 31)) return fail(tiles, S1, upper, "overflow");
+                    // owner of each step, from the work groups' ranges as the kernel forms them
+                    std::vector<int> owner((size_t)ltot, -1);
+                    for (int wi = 0; wi < g1; ++wi) {
+                        const long lbeg = split ? (long)wi * ltot / g1 : (long)wi * S1;
+                        const long lend = split ? (long)(wi + 1) * ltot / g1 : (long)(wi + 1) * S1;
+                        for (long L = lbeg; L < lend; ++L) {
+                            if (owner[L] != -1) return fail(tiles, S1, upper, "step covered twice");
+                            owner[L] = wi;
+                        }
+                    }
+                    for (size_t L = 0; L < owner.size(); ++L)
+                        if (owner[L] < 0) return fail(tiles, S1, upper, "step not covered");
+                    for (int tile = 0; tile < tiles; ++tile) {
+                        const int first = split ? (int)((((long)tile * S1 + 1) * g1 - 1) / ltot) : tile;
+                        const int last = split ? (int)((((long)tile * S1 + S1) * g1 - 1) / ltot) : tile;
+                        // the work groups meeting the tile, in K order
+                        std::vector<int> meet;
+                        for (int k = 0; k < S1; ++k) {
+                            const int w = owner[(size_t)tile * S1 + k];
+                            if (meet.empty() || meet.back() != w) meet.push_back(w);
+                        }
+                        if (meet.front() != first || meet.back() != last || (int)meet.size() != last - first + 1)
+                            return fail(tiles, S1, upper, "contributors");
+                        for (size_t i = 1; i < meet.size(); ++i)
+                            if (meet[i] != meet[i - 1] + 1) return fail(tiles, S1, upper, "contributors not consecutive");
+                        if ((int)meet.size() > kMaxContrib) return fail(tiles, S1, upper, "too many contributors");
+                        if (meet.size() > 1 && tile >= kMaxSplitTiles)
+                            return fail(tiles, S1, upper, "cut-tile counter out of range");
+                    }
+                    ++plans;
+                }
+            }
+    std::printf("ok %ld\n", plans);
+    return 0;
+}

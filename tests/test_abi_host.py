@@ -335,3 +335,21 @@ def test_missing_library_fails_loudly():
     p = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, cwd=root)
     assert p.returncode == 0, p.stderr
     assert p.stdout.startswith("raised:") and "not built" in p.stdout
+
+
+def test_gate_up_split_covers_every_step_once(tmp_path):
+    """The gate/up work split the kernels use (gate_up_groups and the share
+    arithmetic of k_expert, compiled from the kernel header into a host program):
+    over tile counts 1 .. 808, K step counts 1 .. 512 and both kernels' bounds, every
+    (tile, K step) is covered by exactly one work group, each cut tile's computed
+    contributors are exactly the work groups meeting it (consecutive, at most
+    kMaxContrib, the finaliser last), and the arithmetic stays below 2^31."""
+    exe = str(tmp_path / "gate_up_plan_check")
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    import subprocess
+    r = subprocess.run([hipcc, "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+                        os.path.join(ROOT, "tests", "c", "gate_up_plan_check.cpp"), "-o", exe],
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout
+    r = subprocess.run([exe], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.startswith("ok "), r.stdout
