@@ -949,13 +949,12 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) 
 
     // The pass's units and gate/up work groups.  The per-slot kernel's are the
     // host's (one unit per slot).  The deduplicating kernel's real units, one per
-    // distinct expert, are known on the device only: the host sized the grid for
-    // min(n m, N) routed units, and every work group counts the U distinct experts
-    // (the ids are loaded once into LDS) and takes its role among U routed units
-    // (at least one, so a pass without valid ids still writes y) and the shared
-    // experts: gate/up shares over their tiles (gate_up_groups is non-decreasing, so
-    // they never outnumber the host's), then their down items, and the work groups
-    // left over at the end of the grid exit.
+    // distinct expert, are known on the device only: the host sized the grid for the
+    // largest pass any U up to min(n m, N) could give, and every work group counts
+    // the U distinct experts (the ids are loaded once into LDS) and takes its role
+    // among U routed units (at least one, so a pass without valid ids still writes
+    // y) and the shared experts: gate/up shares over their tiles, then their down
+    // items, and the work groups left over at the end of the grid exit.
     int units = a.units, units_r = a.units_r, g1 = a.g1;
     if (MODE == kDedup || want_status) {
         load_ids<NT * RB>(a, sm, want_status);

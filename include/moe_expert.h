@@ -127,10 +127,12 @@ int moe_route_group(const int32_t* ids, int32_t n, int32_t m, int32_t N, int32_t
  * routed slots, then one per token and shared expert) the workspace holds 224 KB
  * of synchronisation counters (one per 128-byte line), the slots' hidden
  * activations (S*d_ff*4 bytes), their expert outputs (S*P*d_model*4 bytes, P = 1..4
- * parts of the d_ff contraction; P > 1 only for passes with few down-projection
- * work items and d_ff too long to keep in registers) and, when the
- * pass's gate/up work is fewer than 511 row tiles, the partial sums of tiles that
- * work groups share (3*S*d_ff*8 bytes), each piece aligned to 256 bytes.  The
+ * parts of the d_ff contraction; P > 1 only for passes that may stream their
+ * down-projection work with fewer than 4 items per compute unit) and, when the
+ * pass's gate/up work may be cut between work groups (per-slot: fewer than 512
+ * row tiles; deduplicating: any pass, since it plans for the experts it finds),
+ * the partial sums of tiles that work groups share (3*S*d_ff*8 bytes), each piece
+ * aligned to 256 bytes.  The
  * size returned is the largest over k = 1..n, so a workspace sized for n serves
  * every smaller n of the same layer.  d_model is limited to 16384. */
 size_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t n, int32_t kind);
