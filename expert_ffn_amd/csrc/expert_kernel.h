@@ -383,8 +383,8 @@ __host__ __device__ inline int gate_up_groups(int tiles, int S1, bool split_ok, 
 
 // Down items of a pass of `units` units whose gate/up work takes g1 work groups: in
 // register mode (rbr row blocks an item, the whole d_ff contraction) when it is
-// allowed and either its items hold 32 rows (rbr = 2, as many rows as a streaming
-// item) or the pass's work groups, the g1 and these items, number at most reg_wgs
+// allowed and either its items hold 32 or 64 rows (rbr >= 2, at least a streaming
+// item's rows) or the pass's work groups, the g1 and these items, number at most reg_wgs
 // (about 11/4 rounds of what the compute units hold at once); else streaming (rbs
 // row blocks an item), the d_ff contraction of each (unit, row tile) cut into ks_s
 // parts.  Register-mode items of 16 rows measured slower than streaming items of
@@ -397,7 +397,7 @@ struct DownShape {
 __host__ __device__ inline DownShape down_shape(int units, int g1, int d, bool reg_allowed, int rbr, int rbs,
                                                 int reg_wgs, int ks_s) {
     const int t2r = (d + kTile * rbr - 1) / (kTile * rbr);
-    if (reg_allowed && (rbr == 2 || g1 + units * t2r <= reg_wgs)) return DownShape{1, t2r, 1};
+    if (reg_allowed && (rbr >= 2 || g1 + units * t2r <= reg_wgs)) return DownShape{1, t2r, 1};
     return DownShape{0, (d + kTile * rbs - 1) / (kTile * rbs), ks_s};
 }
 
@@ -617,7 +617,11 @@ __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e,
 // Down items hold all of their W_down rows in registers (register mode, DPF > 0)
 // when a wave's share of the contraction is at most kPF steps: 16 rows (DPF = 1), or,
 // when it is at most kPF / 2 steps, 32 rows in the same registers (DPF = 2: half as
-// many down items, so more of them are resident while gate/up runs).
+// many down items, so more of them are resident while gate/up runs), or 64 rows in
+// twice the registers (DPF = 4: the deduplicating kernel with one token tile, which
+// has no register cap; at 159 VGPRs and AGPRs it keeps 3 waves per SIMD).  Same box,
+// Qwen3 shape x48: 64-row items made the deduplicating kernel 0.4-2.4 us per layer
+// faster at every n (n = 8: 47.6 -> 45.2 us), fewer items paying the fixed latencies.
 constexpr int kPF = 12;
 constexpr int kSL = 4;  // register mode: h staging loads in flight per thread
 
@@ -636,9 +640,9 @@ __device__ __forceinline__ void down_work(const Args& a, Smem<NT * RB>& sm, int&
     constexpr bool PK = LAY == kLayPacked, TL = LAY == kLayTiled;
     constexpr int P = (2 * RB + NT) <= 3 ? 8 : ((2 * RB + NT) <= 6 ? 4 : 2);  // ring depth, as in the kernel
     constexpr int H = P / 2;
-    constexpr int RBR = DPF == 2 ? 2 : 1, RBS = RB;  // row blocks: register mode, streaming
+    constexpr int RBR = DPF == 4 ? 4 : (DPF == 2 ? 2 : 1), RBS = RB;  // row blocks: register mode, streaming
     constexpr int RBM = RBR > RBS ? RBR : RBS;
-    constexpr int PF = DPF == 2 ? kPF / 2 : kPF;     // register mode: W_down steps a wave holds
+    constexpr int PF = DPF >= 2 ? kPF / 2 : kPF;     // register mode: W_down steps a wave holds
     constexpr int RT2 = kTile * (DPF > 0 ? RBR : RBS);  // output rows of a down item
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -759,14 +763,16 @@ __device__ __forceinline__ void down_work(const Args& a, Smem<NT * RB>& sm, int&
                         }
                     }
                 }
+                static_assert(RBR <= 2 * NT * RB, "the reduction array holds 2 NT RB row blocks per wave");
+                f32x4* redf = &sm.red[0][0][0][0];  // [kWaves][RBR][64]
 #pragma unroll
-                for (int rb = 0; rb < RBR; ++rb) sm.red[wave][0][rb][lane] = acc[rb];
+                for (int rb = 0; rb < RBR; ++rb) redf[(wave * RBR + rb) * 64 + lane] = acc[rb];
                 __syncthreads();
                 if (wave < RBR) {
                     const int rb = wave;
-                    f32x4 v = sm.red[0][0][rb][lane];
+                    f32x4 v = redf[rb * 64 + lane];
 #pragma unroll
-                    for (int w = 1; w < kWaves; ++w) v += sm.red[w][0][rb][lane];
+                    for (int w = 1; w < kWaves; ++w) v += redf[(w * RBR + rb) * 64 + lane];
                     const int i0 = t * RT2 + rb * kTile + 4 * q;
                     if (col_ok && i0 < a.d)  // d % 8 == 0: rows i0..i0+3 all valid
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro,
@@ -940,7 +946,7 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) 
     constexpr int P = (2 * RB + NT) <= 3 ? 8 : ((2 * RB + NT) <= 6 ? 4 : 2);
     // down items: row blocks in register mode (RBR: the W_down rows a wave holds),
     // streaming RB like the gate/up items (down_work)
-    constexpr int RBR = DPF == 2 ? 2 : 1, RBS = RB;
+    constexpr int RBR = DPF == 4 ? 4 : (DPF == 2 ? 2 : 1), RBS = RB;
     __shared__ Smem<NT * RB> sm;
     __shared__ int s_last;
     const int tid = threadIdx.x;
@@ -1064,7 +1070,7 @@ struct Plan {
     int g1, S1;  // gate/up work groups, K steps per gate/up tile
     bool split_ok;  // the workspace holds partial sums of split gate/up tiles
     size_t part_off;
-    int dpf;     // down items: 0 streaming, 1 register mode (16 rows), 2 register mode (32 rows);
+    int dpf;     // down items: 0 streaming, 1, 2, 4 register mode (16, 32, 64 rows);
                  // deduplicating kernel: register mode allowed, decided on the device
     int reg_wgs; // most work groups of a pass with register-mode down items
     int down_wgs;  // down work groups of the grid
@@ -1079,6 +1085,13 @@ void launch_lay(const Args& args, const Plan& p, int grid, hipStream_t st) {
     constexpr int step = Fmt<BF16>::kStep;
     // tiled weights have K a multiple of the step in both contractions (check_desc)
     const bool kf = LAY == kLayTiled || (args.d % step == 0 && args.d_ff % step == 0);
+    if constexpr (MODE == kDedup && NT == 1 && RB == 2) {
+        if (kf && p.dpf == 4) {
+            hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, 4, LAY, SH>), dim3(grid), dim3(kThreads), p.lds, st,
+                               args);
+            return;
+        }
+    }
     if (kf && p.dpf == 2)  // (32-row register mode is planned only for whole steps)
         hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, 2, LAY, SH>), dim3(grid), dim3(kThreads), p.lds, st,
                            args);
