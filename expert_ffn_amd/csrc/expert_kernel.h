@@ -618,10 +618,12 @@ __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e,
 // when a wave's share of the contraction is at most kPF steps: 16 rows (DPF = 1), or,
 // when it is at most kPF / 2 steps, 32 rows in the same registers (DPF = 2: half as
 // many down items, so more of them are resident while gate/up runs), or 64 rows in
-// twice the registers (DPF = 4: the deduplicating kernel with one token tile, which
-// has no register cap; at 159 VGPRs and AGPRs it keeps 3 waves per SIMD).  Same box,
-// Qwen3 shape x48: 64-row items made the deduplicating kernel 0.4-2.4 us per layer
-// faster at every n (n = 8: 47.6 -> 45.2 us), fewer items paying the fixed latencies.
+// twice the registers (DPF = 4, one token tile: 153-159 VGPRs and AGPRs, 3 waves per
+// SIMD).  Same box, Qwen3 shape x48: 64-row items made the deduplicating kernel
+// 0.4-2.4 us per layer faster at every n (n = 8: 47.6 -> 45.2 us) and the per-slot
+// kernel, giving up its cap of 4 waves per SIMD for them, 0.2-3.5 us (n = 1 23.6 ->
+// 23.0 us, n = 8 75.9 -> 72.4 us): fewer items pay the fixed latencies of the
+// hand-off.
 constexpr int kPF = 12;
 constexpr int kSL = 4;  // register mode: h staging loads in flight per thread
 
@@ -926,10 +928,11 @@ __device__ __forceinline__ void down_work(const Args& a, Smem<NT * RB>& sm, int&
     }
 }
 
-// The per-slot kernel with down items in registers and one token tile holds its
-// registers to 4 waves per SIMD, so that a small pass's gate/up and down work
-// groups are all resident at once (a performance choice: every wait is on a lower
-// work-group id, so no wait depends on residency).  With streaming down items (long
+// The per-slot kernel with 16- or 32-row down items in registers and one token tile
+// holds its registers to 4 waves per SIMD, so that a small pass's gate/up and down
+// work groups are all resident at once (a performance choice: every wait is on a
+// lower work-group id, so no wait depends on residency); with 64-row items (half as
+// many) it runs at the 3 waves their registers allow, and measured faster so.  With streaming down items (long
 // d_ff) the work groups cannot all be resident anyway, and the cap (more work
 // groups per compute unit, each keeping less in flight) measured slower: a
 // Mixtral-shaped pass at n = 1 took 157 us against 140 us without it.  With 2 or 4
@@ -938,7 +941,7 @@ __device__ __forceinline__ void down_work(const Args& a, Smem<NT * RB>& sm, int&
 // spill): the latency-bound down items of a 32-token tree pass overlap more, 6 %
 // faster than at the 2 waves its registers would otherwise allow.
 template <bool BF16, int MODE, int NT, int RB, bool KF, int DPF, int LAY, bool SH>
-__global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && NT == 1) ? 4 : (NT == 2 ? 3 : 1)) void k_expert(
+__global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && DPF < 4 && NT == 1) ? 4 : (NT == 2 ? 3 : 1)) void k_expert(
     Args a) {
     constexpr bool TL = LAY == kLayTiled;
     // ring depth in steps: operand registers per step are (2*RB + NT) for gate/up
@@ -1085,7 +1088,7 @@ void launch_lay(const Args& args, const Plan& p, int grid, hipStream_t st) {
     constexpr int step = Fmt<BF16>::kStep;
     // tiled weights have K a multiple of the step in both contractions (check_desc)
     const bool kf = LAY == kLayTiled || (args.d % step == 0 && args.d_ff % step == 0);
-    if constexpr (MODE == kDedup && NT == 1 && RB == 2) {
+    if constexpr (NT == 1 && RB == 2) {
         if (kf && p.dpf == 4) {
             hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, 4, LAY, SH>), dim3(grid), dim3(kThreads), p.lds, st,
                                args);

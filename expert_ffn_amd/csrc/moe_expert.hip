@@ -451,9 +451,9 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     const int64_t resident = (int64_t)kCUs * (kind == MOE_KIND_SLOT ? kResidentSlot : kResidentDedup);
     const int wsteps = (s2 + kWaves - 1) / kWaves;  // a wave's share of the down contraction
     const bool kf = d->d_model % step == 0 && d->d_ff % step == 0;
-    // row blocks of a register-mode item: 64 rows for the deduplicating kernel's
-    // one-token-tile variant (no register cap), 32 rows per-slot (held to 128 VGPRs)
-    const int reg_rows = (kf && wsteps <= kPF / 2) ? (kind == MOE_KIND_DEDUP && p.nt == 1 && p.rb == 2 ? 4 : 2) : 1;
+    // row blocks of a register-mode item: 64 rows for the one-token-tile variants, 32
+    // with more token tiles (shared experts at n > 16)
+    const int reg_rows = (kf && wsteps <= kPF / 2) ? (p.nt == 1 && p.rb == 2 ? 4 : 2) : 1;
     p.reg_wgs = (int)(11 * resident / 4);  // (resident is a multiple of 4)
     bool reg_allowed;
     if (kind == MOE_KIND_SLOT && d->n_shared > 0) {
