@@ -619,7 +619,9 @@ __device__ __forceinline__ bool gate_up(const Args& a, Smem<NT * RB>& sm, int e,
 // when it is at most kPF / 2 steps, 32 rows in the same registers (DPF = 2: half as
 // many down items, so more of them are resident while gate/up runs), or 64 rows in
 // twice the registers (DPF = 4, one token tile: 153-159 VGPRs and AGPRs, 3 waves per
-// SIMD).  Same box, Qwen3 shape x48: 64-row items made the deduplicating kernel
+// SIMD); the deduplicating kernel with one token tile also holds 32 rows of up to
+// kPF steps (DPF = 3, the same registers as DPF = 4): DeepSeek-V2-Lite shape dedup
+// 0.8-3.3 us faster at n = 1..4, the per-slot kernel not faster so.  Same box, Qwen3 shape x48: 64-row items made the deduplicating kernel
 // 0.4-2.4 us per layer faster at every n (n = 8: 47.6 -> 45.2 us) and the per-slot
 // kernel, giving up its cap of 4 waves per SIMD for them, 0.2-3.5 us (n = 1 23.6 ->
 // 23.0 us, n = 8 75.9 -> 72.4 us): fewer items pay the fixed latencies of the
@@ -642,9 +644,9 @@ __device__ __forceinline__ void down_work(const Args& a, Smem<NT * RB>& sm, int&
     constexpr bool PK = LAY == kLayPacked, TL = LAY == kLayTiled;
     constexpr int P = (2 * RB + NT) <= 3 ? 8 : ((2 * RB + NT) <= 6 ? 4 : 2);  // ring depth, as in the kernel
     constexpr int H = P / 2;
-    constexpr int RBR = DPF == 4 ? 4 : (DPF == 2 ? 2 : 1), RBS = RB;  // row blocks: register mode, streaming
+    constexpr int RBR = DPF == 4 ? 4 : (DPF == 2 || DPF == 3 ? 2 : 1), RBS = RB;  // row blocks: register mode, streaming
     constexpr int RBM = RBR > RBS ? RBR : RBS;
-    constexpr int PF = DPF >= 2 ? kPF / 2 : kPF;     // register mode: W_down steps a wave holds
+    constexpr int PF = (DPF == 2 || DPF == 4) ? kPF / 2 : kPF;  // register mode: W_down steps a wave holds
     constexpr int RT2 = kTile * (DPF > 0 ? RBR : RBS);  // output rows of a down item
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -941,7 +943,7 @@ __device__ __forceinline__ void down_work(const Args& a, Smem<NT * RB>& sm, int&
 // spill): the latency-bound down items of a 32-token tree pass overlap more, 6 %
 // faster than at the 2 waves its registers would otherwise allow.
 template <bool BF16, int MODE, int NT, int RB, bool KF, int DPF, int LAY, bool SH>
-__global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && DPF < 4 && NT == 1) ? 4 : (NT == 2 ? 3 : 1)) void k_expert(
+__global__ __launch_bounds__(kThreads, (MODE == kPerSlot && (DPF == 1 || DPF == 2) && NT == 1) ? 4 : (NT == 2 ? 3 : 1)) void k_expert(
     Args a) {
     constexpr bool TL = LAY == kLayTiled;
     // ring depth in steps: operand registers per step are (2*RB + NT) for gate/up
@@ -949,7 +951,7 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && DPF > 0 && DPF < 4 &
     constexpr int P = (2 * RB + NT) <= 3 ? 8 : ((2 * RB + NT) <= 6 ? 4 : 2);
     // down items: row blocks in register mode (RBR: the W_down rows a wave holds),
     // streaming RB like the gate/up items (down_work)
-    constexpr int RBR = DPF == 4 ? 4 : (DPF == 2 ? 2 : 1), RBS = RB;
+    constexpr int RBR = DPF == 4 ? 4 : (DPF == 2 || DPF == 3 ? 2 : 1), RBS = RB;
     __shared__ Smem<NT * RB> sm;
     __shared__ int s_last;
     const int tid = threadIdx.x;
@@ -1089,6 +1091,11 @@ void launch_lay(const Args& args, const Plan& p, int grid, hipStream_t st) {
     // tiled weights have K a multiple of the step in both contractions (check_desc)
     const bool kf = LAY == kLayTiled || (args.d % step == 0 && args.d_ff % step == 0);
     if constexpr (NT == 1 && RB == 2) {
+        if (kf && p.dpf == 3) {
+            hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, 3, LAY, SH>), dim3(grid), dim3(kThreads), p.lds, st,
+                               args);
+            return;
+        }
         if (kf && p.dpf == 4) {
             hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, 4, LAY, SH>), dim3(grid), dim3(kThreads), p.lds, st,
                                args);

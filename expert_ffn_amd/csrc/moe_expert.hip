@@ -451,9 +451,12 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     const int64_t resident = (int64_t)kCUs * (kind == MOE_KIND_SLOT ? kResidentSlot : kResidentDedup);
     const int wsteps = (s2 + kWaves - 1) / kWaves;  // a wave's share of the down contraction
     const bool kf = d->d_model % step == 0 && d->d_ff % step == 0;
-    // row blocks of a register-mode item: 64 rows for the one-token-tile variants, 32
-    // with more token tiles (shared experts at n > 16)
-    const int reg_rows = (kf && wsteps <= kPF / 2) ? (p.nt == 1 && p.rb == 2 ? 4 : 2) : 1;
+    // row blocks of a register-mode item: 64 rows (a wave's share at most kPF / 2
+    // steps) or, deduplicating, 32 rows of up to kPF steps for the one-token-tile
+    // variants; 32 or 16 rows with more token tiles (shared experts at n > 16)
+    const bool wide_reg = kf && p.nt == 1 && p.rb == 2;
+    const int reg_rows = (kf && wsteps <= kPF / 2) ? (wide_reg ? 4 : 2) : (wide_reg && kind == MOE_KIND_DEDUP ? 2 : 1);
+    const int reg_dpf = reg_rows == 4 ? 4 : (reg_rows == 2 ? (wsteps <= kPF / 2 ? 2 : 3) : 1);
     p.reg_wgs = (int)(11 * resident / 4);  // (resident is a multiple of 4)
     bool reg_allowed;
     if (kind == MOE_KIND_SLOT && d->n_shared > 0) {
@@ -480,13 +483,13 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     p.T2 = ds.T2;
     p.ks = ds.ks;
     if (kind == MOE_KIND_SLOT) {
-        p.dpf = ds.reg ? reg_rows : 0;
+        p.dpf = ds.reg ? reg_dpf : 0;
         p.down_wgs = p.units * p.T2 * p.ks;
         p.grid = p.g1 + p.down_wgs;
     } else {
         // the device takes the shape for the U distinct experts it finds; the grid
         // covers the largest pass, gate/up and down work groups, over every U
-        p.dpf = reg_allowed ? reg_rows : 0;
+        p.dpf = reg_allowed ? reg_dpf : 0;
         p.grid = 0;
         bool streams = false;
         for (int U = 1; U <= p.units_r; ++U) {
