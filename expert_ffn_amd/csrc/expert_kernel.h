@@ -286,13 +286,13 @@ struct Smem {
 // The pass's ids in LDS (ids out of range as -1) and the presence bitmap of the
 // experts they name; with want_status, sm.id_status is set for ids out of range or
 // repeated within a token (read after the call by thread 0).  Loaded once per work
-// group: the unit selections below read it.  Starts and ends with a barrier.
+// group, at the kernel's start (no earlier use of sm): the unit selections below read
+// it.  Ends with a barrier.
 template <int NB>
 __device__ void load_ids(const Args& a, Smem<NB>& sm, bool want_status) {
     const int tid = threadIdx.x;
     const int nm = a.n * a.m;
     const int nwords = (a.N + 31) >> 5;
-    __syncthreads();  // earlier reads of sm are done
     if (tid < nwords) sm.pres[tid] = 0u;
     if (tid == 0) sm.id_status = 0;
     const int id = tid < nm ? a.ids[tid] : -1;
@@ -314,45 +314,48 @@ __device__ void load_ids(const Args& a, Smem<NB>& sm, bool want_status) {
 // Stable grouping of the pass's slots by expert, from what load_ids left in LDS: the
 // number U of distinct experts and, for distinct expert number `u` (ids in increasing
 // order; u < 0 or u >= U: none), its id e (else -1) and, with `group`, its slots,
-// increasing, in sm.grp[0..g).  Every wave computes the prefix popcount and the
-// ranks itself (and writes all of sm.grp), so no barrier is needed after it; the
-// barrier before it keeps the previous unit's reads of sm.grp ahead of the writes.
+// increasing, in sm.grp[0..g).  One LDS round trip (the presence words and, with
+// `group`, the ids, read together); the walk over the presence words runs on the
+// scalar unit (readlane) and the group is formed with ballots, so the chain of
+// dependent LDS operations a shuffle scan would make stays off the path to the
+// first weight load.  Every wave computes the same result itself (and writes all of
+// sm.grp), so no barrier is needed after it; the barrier before it keeps the
+// previous unit's reads of sm.grp ahead of the writes.
 template <int NB>
 __device__ void select_unit(const Args& a, Smem<NB>& sm, int u, bool group, int& e_out, int& g_out, int& U_out,
                             bool barrier = true) {
+    constexpr int kChunks = MOE_MAX_SLOTS / 64;
     const int lane = threadIdx.x & 63;
     const int nm = a.n * a.m;
-    const int nwords = (a.N + 31) >> 5;
+    const int nwords = (a.N + 31) >> 5;  // <= 32
     if (barrier) __syncthreads();
-    // prefix popcount over the presence words (<= 32 words, lanes 0..31)
     const uint32_t word = lane < nwords ? sm.pres[lane] : 0u;
-    const int c = __popc(word);
-    int incl = c;
+    int idv[kChunks];
 #pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-        const int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
+    for (int i = 0; i < kChunks; ++i) idv[i] = (group && lane + 64 * i < nm) ? sm.ids[lane + 64 * i] : -1;
+    // distinct expert u: the (u - U)-th set bit of the word where the running count U
+    // passes u (words in increasing order, bits in increasing order)
+    int U = 0, e = -1;
+    for (int w = 0; w < nwords; ++w) {
+        uint32_t wv = (uint32_t)__builtin_amdgcn_readlane((int)word, w);
+        const int c = __popc(wv);
+        if (u >= U && u < U + c) {
+            for (int k = u - U; k > 0; --k) wv &= wv - 1u;  // drop the lower set bits
+            e = w * 32 + __ffs(wv) - 1;
+        }
+        U += c;
     }
-    const int U = __shfl(incl, 31, 64);
-    const int excl = incl - c;
-    const bool mine = lane < 32 && u >= excl && u < incl;
-    int cand = -1;
-    if (mine) {
-        uint32_t wv = word;
-        for (int k = u - excl; k > 0; --k) wv &= wv - 1;  // drop the lower set bits
-        cand = lane * 32 + __ffs(wv) - 1;
-    }
-    const unsigned long long mb = __ballot(mine);
-    const int e = mb ? __shfl(cand, __ffsll((long long)mb) - 1, 64) : -1;
     int g = 0;
     if (group && e >= 0) {
+        const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
-        for (int i = 0; i < MOE_MAX_SLOTS / 64; ++i) {
-            const int s = lane + 64 * i;
-            const bool f = s < nm && sm.ids[s] == e;
-            const unsigned long long bal = __ballot(f);
-            if (f) sm.grp[g + __popcll(bal & ((1ull << lane) - 1ull))] = s;
-            g += __popcll(bal);
+        for (int i = 0; i < kChunks; ++i) {
+            if (64 * i < nm) {
+                const bool f = idv[i] == e;
+                const unsigned long long bal = __ballot(f);
+                if (f) sm.grp[g + __popcll(bal & below)] = lane + 64 * i;
+                g += __popcll(bal);
+            }
         }
     }
     e_out = e;
