@@ -292,10 +292,12 @@ template <int NB>
 __device__ void load_ids(const Args& a, Smem<NB>& sm, bool want_status) {
     const int tid = threadIdx.x;
     const int nm = a.n * a.m;
+    // the id load first, so that the kernel-argument loads it depends on go out
+    // together at the kernel's start
+    const int id = tid < nm ? a.ids[tid] : -1;
     const int nwords = (a.N + 31) >> 5;
     if (tid < nwords) sm.pres[tid] = 0u;
     if (tid == 0) sm.id_status = 0;
-    const int id = tid < nm ? a.ids[tid] : -1;
     const bool valid = tid < nm && id >= 0 && id < a.N;
     if (tid < nm) sm.ids[tid] = valid ? id : -1;
     __syncthreads();
