@@ -1080,8 +1080,9 @@ struct Plan {
     int g1, S1;  // gate/up work groups, K steps per gate/up tile
     bool split_ok;  // the workspace holds partial sums of split gate/up tiles
     size_t part_off;
-    int dpf;     // down items: 0 streaming, 1, 2, 4 register mode (16, 32, 64 rows);
-                 // deduplicating kernel: register mode allowed, decided on the device
+    int dpf;     // down items: 0 streaming, 1, 2, 4 register mode (16, 32, 64 rows), 3 register
+                 // mode (32 rows of up to kPF steps); deduplicating kernel: register mode
+                 // allowed, decided on the device
     int reg_wgs; // most work groups of a pass with register-mode down items
     int down_wgs;  // down work groups of the grid
     int grid;      // work groups of the launch
@@ -1095,14 +1096,18 @@ void launch_lay(const Args& args, const Plan& p, int grid, hipStream_t st) {
     constexpr int step = Fmt<BF16>::kStep;
     // tiled weights have K a multiple of the step in both contractions (check_desc)
     const bool kf = LAY == kLayTiled || (args.d % step == 0 && args.d_ff % step == 0);
-    if constexpr (NT == 1 && RB == 2) {
-        if (kf && p.dpf == 3) {
-            hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, 3, LAY, SH>), dim3(grid), dim3(kThreads), p.lds, st,
+    // 64-row register items: one token tile, or two in the deduplicating kernel
+    // (groups of up to 32 tokens, staged in chunks)
+    if constexpr ((NT == 1 || (NT == 2 && MODE == kDedup)) && RB == 2) {
+        if (kf && p.dpf == 4) {
+            hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, 4, LAY, SH>), dim3(grid), dim3(kThreads), p.lds, st,
                                args);
             return;
         }
-        if (kf && p.dpf == 4) {
-            hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, 4, LAY, SH>), dim3(grid), dim3(kThreads), p.lds, st,
+    }
+    if constexpr (NT == 1 && RB == 2) {
+        if (kf && p.dpf == 3) {
+            hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, 3, LAY, SH>), dim3(grid), dim3(kThreads), p.lds, st,
                                args);
             return;
         }

@@ -430,11 +430,17 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     p.g1 = gate_up_groups((int)tiles, p.S1, p.split_ok, kind == MOE_KIND_SLOT ? 2 * kCUs : kDedupSplitUpper);
     const bool split = p.g1 != tiles;
     // Down items in register mode: when a wave's share of the down contraction fits
-    // kPF steps, and one LDS chunk of at most 16 tokens (one MFMA column tile) holds a
-    // whole group (several chunks would serialise their h loads and O stores; a
-    // per-slot pass with shared experts stages their n tokens in chunks of what
-    // kHsBudgetShared holds), and the pass's work groups (gate/up, then register-mode
-    // down items) fill at most 11/4 rounds of what the compute units hold at once.
+    // kPF steps and one token's h fits the LDS staging budget, and the pass's work
+    // groups (gate/up, then register-mode down items) fill at most 11/4 rounds of
+    // what the compute units hold at once.  h is staged gl tokens at a time (at most
+    // 16, one MFMA column tile); a larger group runs its chunks one after another
+    // on the same W_down registers (h loads, products, O stores in series).  A
+    // per-slot pass stages one token (its shared experts' n tokens in chunks of what
+    // kHsBudgetShared holds); a deduplicating pass up to what kHsBudget holds.
+    // Same-box, the 32-node tree on the Qwen3 shape (groups of up to 32 tokens, two
+    // token tiles): 64-row register items 146 us per pass against 164 us streaming
+    // (32-row register items: 167 us); the DeepSeek-V2-Lite shape's dedup passes at
+    // n = 6..8, which now stage 5 tokens a chunk, are unchanged.
     // Register-mode items prefetch their W_down while they wait, which pays for those
     // resident during gate/up; items dispatched after it run in rounds of short,
     // latency-bound work, where streaming items (twice the rows, a load ring) do
@@ -452,10 +458,11 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     const int wsteps = (s2 + kWaves - 1) / kWaves;  // a wave's share of the down contraction
     const bool kf = d->d_model % step == 0 && d->d_ff % step == 0;
     // row blocks of a register-mode item: 64 rows (a wave's share at most kPF / 2
-    // steps) or, deduplicating, 32 rows of up to kPF steps for the one-token-tile
-    // variants; 32 or 16 rows with more token tiles (shared experts at n > 16)
+    // steps; one token tile, or two in the deduplicating kernel) or, deduplicating,
+    // 32 rows of up to kPF steps for the one-token-tile variants; else 32 or 16 rows
     const bool wide_reg = kf && p.nt == 1 && p.rb == 2;
-    const int reg_rows = (kf && wsteps <= kPF / 2) ? (wide_reg ? 4 : 2) : (wide_reg && kind == MOE_KIND_DEDUP ? 2 : 1);
+    const bool reg64 = wide_reg || (kf && p.nt == 2 && p.rb == 2 && kind == MOE_KIND_DEDUP);
+    const int reg_rows = (kf && wsteps <= kPF / 2) ? (reg64 ? 4 : 2) : (wide_reg && kind == MOE_KIND_DEDUP ? 2 : 1);
     const int reg_dpf = reg_rows == 4 ? 4 : (reg_rows == 2 ? (wsteps <= kPF / 2 ? 2 : 3) : 1);
     p.reg_wgs = (int)(11 * resident / 4);  // (resident is a multiple of 4)
     bool reg_allowed;
@@ -464,8 +471,9 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
         reg_allowed = wsteps <= kPF && (int64_t)per_tok <= kHsBudget;
         p.gl = reg_allowed ? std::min(n, std::min(cap, 16)) : 0;
     } else {
-        reg_allowed = wsteps <= kPF && gmax <= 16 && (int64_t)per_tok * gmax <= kHsBudget;
-        p.gl = reg_allowed ? gmax : 0;
+        const int cap = (int)std::max<int64_t>(1, kHsBudget / per_tok);
+        reg_allowed = wsteps <= kPF && (int64_t)per_tok <= kHsBudget;
+        p.gl = reg_allowed ? std::min(gmax, std::min(cap, 16)) : 0;
     }
     // Streaming down items (not register mode) each stream their rows' W_down after
     // the wait, at what one work group keeps in flight; with fewer than 4 items per
