@@ -272,6 +272,14 @@ __device__ __forceinline__ int slot_tok(const Args& a, int slot) {
     return slot < nm ? slot / a.m : (slot - nm) % a.n;
 }
 
+// LDS bytes for the h a register-mode down item stages (gl tokens of a chunk).
+// Variants whose cross-wave reduction array holds at least that much (two or more
+// token tiles: 32 KB) stage h in that array itself, which no other part of a down
+// item uses while h is read, and need no dynamic LDS: a dedup pass of the 32-node
+// tree then keeps 3 work groups per compute unit (its registers' limit) instead of 2.
+constexpr int kHsBudget = 32 * 1024;
+__host__ __device__ constexpr bool hs_in_red(int nb) { return 16 * kWaves * 2 * nb * 64 >= kHsBudget; }
+
 template <int NB>
 struct Smem {
     f32x4 red[kWaves][2][NB][64];  // cross-wave reduction of the MFMA accumulators (NB = row blocks x token tiles)
@@ -715,7 +723,10 @@ __device__ __forceinline__ void down_work(const Args& a, Smem<NT * RB>& sm, int&
             // wait, h is staged in LDS `gl` tokens at a time (one cooperative
             // sc1 load per chunk) and the products run from registers and LDS,
             // for any group size with one read of the weights.
-            extern __shared__ __align__(16) char hs[];  // [gl][hi row, lo row], padded rows
+            extern __shared__ __align__(16) char hs_dyn[];
+            constexpr bool HSR = hs_in_red(NT * RB);
+            static_assert(!HSR || sizeof(sm.red) >= kHsBudget, "h staged in the reduction array");
+            char* const hs = HSR ? reinterpret_cast<char*>(&sm.red[0][0][0][0]) : hs_dyn;  // [gl][hi row, lo row], padded rows
             u32x4 pa[PF][RBR];
 #pragma unroll
             for (int i = 0; i < PF; ++i)
@@ -774,6 +785,7 @@ __device__ __forceinline__ void down_work(const Args& a, Smem<NT * RB>& sm, int&
                 }
                 static_assert(RBR <= 2 * NT * RB, "the reduction array holds 2 NT RB row blocks per wave");
                 f32x4* redf = &sm.red[0][0][0][0];  // [kWaves][RBR][64]
+                if constexpr (HSR) __syncthreads();  // every wave's reads of h are done before redf overwrites it
 #pragma unroll
                 for (int rb = 0; rb < RBR; ++rb) redf[(wave * RBR + rb) * 64 + lane] = acc[rb];
                 __syncthreads();

@@ -391,7 +391,6 @@ int check_desc(const moe_layer_desc* d, int32_t n) {
 // work groups per compute unit at once: the per-slot register-mode kernel's launch
 // bound, and what the deduplicating kernel's registers allow
 constexpr int kResidentSlot = 4, kResidentDedup = 3;
-constexpr int kHsBudget = 32 * 1024;  // LDS bytes for staged h (down items in register mode)
 // per-slot passes with shared experts: LDS for the shared experts' h chunks
 constexpr int kHsBudgetShared = 12 * 1024;
 
@@ -511,7 +510,8 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
         p.ks = streams ? ks_s : 1;  // O holds the streaming form's parts if it may stream
     }
     if (!p.dpf) p.gl = 0;
-    p.lds = p.dpf ? (size_t)p.gl * per_tok : 0;
+    // (h staged in the reduction array when it holds kHsBudget: no dynamic LDS)
+    p.lds = (p.dpf && !hs_in_red(p.nt * p.rb)) ? (size_t)p.gl * per_tok : 0;
     p.sync_off = 0;
     p.h_off = (size_t)kSyncWords * 4;
     p.o_off = p.h_off + align_up((size_t)p.nslot * d->d_ff * 4);
