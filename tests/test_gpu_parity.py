@@ -341,6 +341,18 @@ def test_qwen3_layer_zipf_and_tree(layout):
     x = synth.pass_x(spec, 77, 3, 500, 32)
     say("tree pass n=32, every token")
     _compare(dl, x, ttr.ids, ttr.w, "tree")
+    # 32 tokens sharing one expert (a group of 32: the deduplicating kernel stages its
+    # h in several chunks) and every other token a second one (a group of 16)
+    rng = np.random.default_rng(78)
+    ids = np.empty((32, spec.m), np.int32)
+    for t in range(32):
+        rest = rng.choice(np.arange(2, spec.N), spec.m - 2, replace=False)
+        ids[t] = np.concatenate(([0, 1 if t % 2 == 0 else int(rng.integers(2, spec.N))], rest))
+        while len(set(ids[t].tolist())) < spec.m:
+            ids[t, 1] = int(rng.integers(2, spec.N))
+    w = rng.random((32, spec.m)).astype(np.float32)
+    say("n=32 pass with groups of 32 and 16 tokens")
+    _compare(dl, synth.pass_x(spec, 77, 3, 501, 32), ids, w, "large groups")
 
 
 @pytest.mark.parametrize("kind", ["uniform", "correlated"])
