@@ -380,14 +380,15 @@ __device__ void select_unit(const Args& a, Smem<NB>& sm, int u, bool group, int&
 // room for partial sums).  Non-decreasing in `tiles` (upper >= kCUs).
 // upper: 2 kCUs for the per-slot kernel, kDedupSplitUpper for the deduplicating one.
 // Same box, Qwen3-shaped layer x48 (zipf) and DeepSeek-V2-Lite-shaped layer, 8 windows
-// per n, two rounds agreeing within 0.1 us: the deduplicating kernel is 1-4 us per
-// layer faster at n = 3..8 and 0.9-3 us at n = 2 when it cuts only below 288 tiles
-// (against 320, 384, 512); the per-slot kernel's 384-tile pass (Qwen3 shape, n = 2)
-// is 3.2 us faster cut (29.8 against 33.0 us).  A work group's own stream is bounded
-// by the loads it keeps in flight, so one work group per tile keeps more bytes in
-// flight; below ~288 tiles the compute units with two tiles finish last by a whole
-// tile, and the cut wins.
-constexpr int kDedupSplitUpper = 288;
+// per n, two rounds agreeing within 0.1 us: the deduplicating kernel cutting below
+// 320 tiles against 288 is 0.3 us per layer faster at n = 2 (Qwen3, 12-13 distinct
+// experts: 288 or 312 tiles) and the same elsewhere; below 512 it is 1-2.7 us slower
+// at n = 3..8; the per-slot kernel's 384-tile pass (Qwen3 shape, n = 2) is 3.2 us
+// faster cut (29.8 against 33.0 us).  A work group's own stream is bounded by the
+// loads it keeps in flight, so one work group per tile keeps more bytes in flight;
+// below ~300 tiles the compute units with two tiles finish last by a whole tile, and
+// the cut wins.
+constexpr int kDedupSplitUpper = 320;
 __host__ __device__ inline int gate_up_groups(int tiles, int S1, bool split_ok, int upper) {
     const bool few = tiles * 2 < kCUs && S1 >= 2;
     const bool split = ((tiles * 2 >= kCUs && tiles < upper) || few) && split_ok;
@@ -956,9 +957,10 @@ __device__ __forceinline__ void down_work(const Args& a, Smem<NT * RB>& sm, int&
 // groups per compute unit, each keeping less in flight) measured slower: a
 // Mixtral-shaped pass at n = 1 took 157 us against 140 us without it.  With 2 or 4
 // token tiles (shared experts, n > 16) the cap made the kernel spill.  With 2 token
-// tiles (passes of 17..32 tokens) the kernel is held to 3 waves per SIMD (3-4 VGPRs
-// spill): the latency-bound down items of a 32-token tree pass overlap more, 6 %
-// faster than at the 2 waves its registers would otherwise allow.
+// tiles (passes of 17..32 tokens) the kernel is held to 3 waves per SIMD (no VGPR
+// spills for whole K steps, 3-11 for a ragged K): the latency-bound down items of a
+// 32-token tree pass overlap more, 6 % faster than at the 2 waves its registers
+// would otherwise allow.
 template <bool BF16, int MODE, int NT, int RB, bool KF, int DPF, int LAY, bool SH>
 __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && (DPF == 1 || DPF == 2) && NT == 1) ? 4 : (NT == 2 ? 3 : 1)) void k_expert(
     Args a) {
