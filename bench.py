@@ -443,6 +443,24 @@ def write_sq_summary(csv_a, csv_b, pass_json, out_dir=None):
     return path
 
 
+def launch_gaps(disp):
+    """Launch gaps of the expert kernels from kernel-trace dispatches (start ns, end ns,
+    name): for every pair of dispatches adjacent in start order that are launches of
+    the same k_expert kernel (a pass's layers back to back), the idle time from the
+    first's end to the second's start.  Returns {kernel: (gaps, gap ns, busy ns)},
+    busy = the durations of the dispatches that follow a gap."""
+    import re
+    out = {}
+    disp = sorted(disp)
+    for (s0, e0, k0), (s1, e1, k1) in zip(disp, disp[1:]):
+        m0, m1 = re.search(r"k_expert<[^>]*>", k0), re.search(r"k_expert<[^>]*>", k1)
+        if not m0 or not m1 or m0.group(0) != m1.group(0):
+            continue
+        n, g, busy = out.get(m0.group(0), (0, 0, 0))
+        out[m0.group(0)] = (n + 1, g + max(0, s1 - e0), busy + (e1 - s1))
+    return out
+
+
 def write_profile_summary(prof_dir, bench_json):
     """profiles/k_expert_qwen3x48.md: short summary of a `rocprofv3 --kernel-trace
     --stats` run of this bench on the headline workload, with the bench line's event
@@ -452,12 +470,15 @@ def write_profile_summary(prof_dir, bench_json):
     trace = [f for f in os.listdir(prof_dir) if f.endswith("kernel_trace.csv")][0]
     stats = [f for f in os.listdir(prof_dir) if f.endswith("kernel_stats.csv")][0]
     d = collections.defaultdict(list)
+    disp = []  # (start, end, kernel) of every dispatch, for the launch gaps
     for r in _counter_rows(os.path.join(prof_dir, trace)):
+        disp.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
         m = re.search(r"(k_\w+)(<[^>]*>)?", r["Kernel_Name"])
         if not m:
             continue
         key = (m.group(1) + (m.group(2) or ""), int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
         d[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000)
+    gaps = launch_gaps(disp)
     b = [json.loads(l) for l in open(bench_json) if l.startswith('{"metric"')][-1]
     lines = ["# k_expert (per-slot and deduplicating), qwen3-shaped layer x48 per pass, zipf routing, n = 1..8",
              "", "Command (from the repository root, one MI355X):", "", "```", PROF_CMD, "```", "",
@@ -484,7 +505,14 @@ def write_profile_summary(prof_dir, bench_json):
                          kernel, kk["avg_launch_us"], sum(tr) / max(len(tr), 1), len(tr),
                          kk["bytes_per_launch"], kk["achieved"], kk["frac"]))
     lines += ["- value: %.1f GB/s (all passes, both kernels); roofline kernel: %s" % (b["value"], rf["kernel"]),
-              "- source hash %s" % b.get("source_hash")]
+              "- source hash %s" % b.get("source_hash"), "",
+              "## Launch gaps (kernel trace)", "",
+              "Launches of one kernel back to back in a pass (one launch per layer, 48 per pass): the idle time",
+              "between one launch's end and the next one's start, over the busy time plus those gaps.", "",
+              "| kernel | gaps | mean gap us | launch-gap share |", "|---|---|---|---|"]
+    for name, (n_gap, gap_ns, busy_ns) in sorted(gaps.items()):
+        lines.append("| `%s` | %d | %.2f | %.4f |" % (name, n_gap, gap_ns / max(n_gap, 1) / 1000,
+                                                     gap_ns / max(gap_ns + busy_ns, 1)))
     path = os.path.join(ROOT, "profiles", "k_expert_%s.md" % HEADLINE)
     open(path, "w").write("\n".join(lines) + "\n")
     print(path)

@@ -7,6 +7,8 @@
   summed over windows; the crossover as the smallest n from which the saving stays
   positive; both against records computed by hand.
 * The final line: compact (a few KB), with the fields the metric needs.
+* Launch gaps from a kernel trace: idle time between back-to-back launches of one
+  expert kernel, against a hand-made trace.
 """
 import csv
 import json
@@ -168,3 +170,18 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=60)
     assert p.returncode == 2
     assert "one GPU" in p.stderr and p.stdout == ""
+
+
+def test_launch_gaps_between_back_to_back_expert_launches():
+    """Gaps count only between adjacent launches of the same expert kernel, in start
+    order; another kernel in between (the flush) breaks the run."""
+    a = "void moe_k::k_expert<true, 0, 1, 2, true, 4, 2, false>(moe_k::Args)"
+    b = "void moe_k::k_expert<true, 1, 1, 2, true, 4, 2, false>(moe_k::Args)"
+    flush = "void at::native::reduce_kernel<512, 1>(...)"
+    disp = [(100, 200, a), (210, 300, a), (330, 400, a),   # gaps 10 and 30; busy 90 + 70
+            (400, 900, flush),
+            (905, 1000, a),                                # after the flush: no gap counted
+            (1000, 1100, b), (1100, 1150, b)]              # gap 0; busy 50
+    g = bench.launch_gaps(list(reversed(disp)))            # (any input order)
+    ka, kb = "k_expert<true, 0, 1, 2, true, 4, 2, false>", "k_expert<true, 1, 1, 2, true, 4, 2, false>"
+    assert g == {ka: (2, 40, 160), kb: (1, 0, 50)}
