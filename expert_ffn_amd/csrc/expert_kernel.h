@@ -395,6 +395,39 @@ __host__ __device__ inline int gate_up_groups(int tiles, int S1, bool split_ok, 
     return !split ? tiles : (few ? 2 * tiles : kCUs);
 }
 
+// Remainder cut, for large tiles (kCutMinS1 K steps or more, where one more whole
+// tile on a compute unit costs tens of microseconds) in passes of `upper` tiles or
+// more: the whole rounds of kCUs tiles one work group each, then the remaining
+// tiles' K steps cut into min(kCUs, 2 rem) equal contiguous shares, each at least
+// half a tile, so that a tile meets at most kMaxContrib shares.  Below `upper` the
+// rule of gate_up_groups.  Only the kernels built with RC apply it (a separate
+// variant: the others' code is unchanged).
+constexpr int kCutMinS1 = 128;
+__host__ __device__ inline int rc_whole(int tiles) { return kCUs * (tiles / kCUs); }
+__host__ __device__ inline int gate_up_groups_rc(int tiles, int S1, bool split_ok, int upper) {
+    if (!split_ok || tiles < upper || S1 < 2) return gate_up_groups(tiles, S1, split_ok, upper);
+    const int rem = tiles - rc_whole(tiles);
+    return rem == 0 ? tiles : rc_whole(tiles) + (2 * rem < kCUs ? 2 * rem : kCUs);
+}
+// A pass planned by gate_up_groups_rc with a remainder (g1 != tiles, tiles >= upper):
+// work group wi's share [lbeg, lend) of the (tile, K step) space, and a tile's
+// contributors first .. last (whole tiles: the one work group; a remainder tile:
+// the shares that meet it, in K order, the finaliser last).  A cut tile's counter
+// is its index among the remainder tiles, tile - W < kCUs.
+struct RcPlan {
+    int S1, W, G2, Lr;  // whole-tile work groups, remainder shares, remainder K steps
+    __host__ __device__ RcPlan(int tiles, int s1, int g1)
+        : S1(s1), W(rc_whole(tiles)), G2(g1 - rc_whole(tiles)), Lr((tiles - rc_whole(tiles)) * s1) {}
+    __host__ __device__ int lbeg(int wi) const { return wi < W ? wi * S1 : W * S1 + (wi - W) * Lr / G2; }
+    __host__ __device__ int lend(int wi) const { return wi < W ? (wi + 1) * S1 : W * S1 + (wi - W + 1) * Lr / G2; }
+    __host__ __device__ int first(int tile) const {
+        return tile < W ? tile : W + (((tile - W) * S1 + 1) * G2 - 1) / Lr;
+    }
+    __host__ __device__ int last(int tile) const {
+        return tile < W ? tile : W + (((tile - W) * S1 + S1) * G2 - 1) / Lr;
+    }
+};
+
 // Down items of a pass of `units` units whose gate/up work takes g1 work groups: in
 // register mode (rbr row blocks an item, the whole d_ff contraction) when it is
 // allowed and either its items hold 32 or 64 rows (rbr >= 2, at least a streaming
@@ -961,7 +994,8 @@ __device__ __forceinline__ void down_work(const Args& a, Smem<NT * RB>& sm, int&
 // spills for whole K steps, 3-11 for a ragged K): the latency-bound down items of a
 // 32-token tree pass overlap more, 6 % faster than at the 2 waves its registers
 // would otherwise allow.
-template <bool BF16, int MODE, int NT, int RB, bool KF, int DPF, int LAY, bool SH>
+// RC: the remainder cut of large tiles (gate_up_groups_rc), a variant of its own.
+template <bool BF16, int MODE, int NT, int RB, bool KF, int DPF, int LAY, bool SH, bool RC = false>
 __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && (DPF == 1 || DPF == 2) && NT == 1) ? 4 : (NT == 2 ? 3 : 1)) void k_expert(
     Args a) {
     constexpr bool TL = LAY == kLayTiled;
@@ -994,7 +1028,8 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && (DPF == 1 || DPF == 
         if (MODE == kDedup) {
             units_r = max(U, 1);
             units = units_r + (SH ? a.n_shared : 0);
-            g1 = gate_up_groups(units * a.T1, a.S1, a.split_ok, kDedupSplitUpper);
+            g1 = RC ? gate_up_groups_rc(units * a.T1, a.S1, a.split_ok, kDedupSplitUpper)
+                    : gate_up_groups(units * a.T1, a.S1, a.split_ok, kDedupSplitUpper);
         }
         if (want_status && tid == 0) {
             a.info[0] = U;
@@ -1051,6 +1086,10 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && (DPF == 1 || DPF == 
         // g1 <= kMaxSplitTiles.
         const int tiles = units * a.T1;
         const bool split = g1 != tiles;
+        // RC variants, from the kernel's bound of tiles on: the remainder cut (RcPlan;
+        // its arithmetic also stays under 2^31)
+        const bool rcm = RC && split && tiles >= (MODE == kPerSlot ? 2 * kCUs : kDedupSplitUpper);
+        const RcPlan rp(tiles, a.S1, g1);
         const int ltot = tiles * a.S1;
         const int wi = blockIdx.x;
         // (integer divisions run on the vector unit: readfirstlane keeps the
@@ -1059,10 +1098,10 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && (DPF == 1 || DPF == 
         // of a split tile (it contributes without waiting) and its first is the
         // tail of one (it finalises, waiting on lower work-group ids).  In this
         // order no wait depends on another wait.
-        const int lbeg = uni(split ? wi * ltot / g1 : wi * a.S1);
+        const int lbeg = uni(rcm ? rp.lbeg(wi) : (split ? wi * ltot / g1 : wi * a.S1));
         int cur = -1, e = -1, g = 0;
         bool sh = false;
-        for (int L = uni(split ? (wi + 1) * ltot / g1 : (wi + 1) * a.S1); L > lbeg;) {
+        for (int L = uni(rcm ? rp.lend(wi) : (split ? (wi + 1) * ltot / g1 : (wi + 1) * a.S1)); L > lbeg;) {
             const int tile = uni((L - 1) / a.S1);
             const int k1 = L - tile * a.S1;
             const int k0 = max(0, lbeg - tile * a.S1);
@@ -1074,9 +1113,11 @@ __global__ __launch_bounds__(kThreads, (MODE == kPerSlot && (DPF == 1 || DPF == 
             }
             if (g == 0) continue;
             // work groups whose shares meet this tile: first .. last
-            const int first = uni(split ? ((tile * a.S1 + 1) * g1 - 1) / ltot : wi);
-            const int last = uni(split ? ((tile * a.S1 + a.S1) * g1 - 1) / ltot : wi);
-            const bool fin = gate_up<BF16, NT, RB, KF, P, SH, TL>(a, sm, e, sh, g, t, k0, k1, tile,
+            const int first = uni(rcm ? rp.first(tile) : (split ? ((tile * a.S1 + 1) * g1 - 1) / ltot : wi));
+            const int last = uni(rcm ? rp.last(tile) : (split ? ((tile * a.S1 + a.S1) * g1 - 1) / ltot : wi));
+            // (a cut tile's counter: its index among the cut tiles)
+            const int ctile = rcm ? (tile < rp.W ? 0 : tile - rp.W) : tile;
+            const bool fin = gate_up<BF16, NT, RB, KF, P, SH, TL>(a, sm, e, sh, g, t, k0, k1, ctile,
                                                               last - first + 1, wi - first);
             if (tid == 0 && fin) atomicAdd(a.sync + kLine * u, 1);  // h-ready count of unit u
         }
@@ -1097,6 +1138,7 @@ struct Plan {
     int dpf;     // down items: 0 streaming, 1, 2, 4 register mode (16, 32, 64 rows), 3 register
                  // mode (32 rows of up to kPF steps); deduplicating kernel: register mode
                  // allowed, decided on the device
+    bool rc;     // gate/up tiles: the remainder cut (gate_up_groups_rc, kernel variant RC)
     int reg_wgs; // most work groups of a pass with register-mode down items
     int down_wgs;  // down work groups of the grid
     int grid;      // work groups of the launch
@@ -1110,6 +1152,15 @@ void launch_lay(const Args& args, const Plan& p, int grid, hipStream_t st) {
     constexpr int step = Fmt<BF16>::kStep;
     // tiled weights have K a multiple of the step in both contractions (check_desc)
     const bool kf = LAY == kLayTiled || (args.d % step == 0 && args.d_ff % step == 0);
+    // the remainder cut: planned only for bf16 passes of large tiles with streaming
+    // down items, one token tile and no shared experts
+    if constexpr (BF16 && NT == 1 && RB == 2 && !SH) {
+        if (kf && p.rc && p.dpf == 0) {
+            hipLaunchKernelGGL((k_expert<BF16, MODE, NT, RB, true, 0, LAY, SH, true>), dim3(grid), dim3(kThreads), 0,
+                               st, args);
+            return;
+        }
+    }
     // 64-row register items: one token tile, or two in the deduplicating kernel
     // (groups of up to 32 tokens, staged in chunks)
     if constexpr ((NT == 1 || (NT == 2 && MODE == kDedup)) && RB == 2) {

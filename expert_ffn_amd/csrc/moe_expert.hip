@@ -422,11 +422,24 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     // (gate_up_groups; the deduplicating kernel applies the same rule on the device
     // to its real units, U of the min(n m, N) planned here, and may cut tiles where
     // this plan does not: its workspace always holds the partial sums)
+    // Large tiles (kCutMinS1 K steps or more: the Mixtral shape's 512 KB tiles) with
+    // streaming down items take the remainder cut instead above the bound
+    // (gate_up_groups_rc: whole rounds of kCUs tiles, the remainder cut into shares),
+    // in a kernel variant of its own; bf16, one token tile, no shared experts.
     p.S1 = (d->d_model + step - 1) / step;
     const int64_t tiles = (int64_t)p.units * p.T1;
     const int64_t part_bytes = (int64_t)kMaxContrib * p.nslot * d->d_ff * 8;
     p.split_ok = part_bytes <= (64ll << 20);
-    p.g1 = gate_up_groups((int)tiles, p.S1, p.split_ok, kind == MOE_KIND_SLOT ? 2 * kCUs : kDedupSplitUpper);
+    const int s2 = (d->d_ff + step - 1) / step;
+    const int wsteps = (s2 + kWaves - 1) / kWaves;  // a wave's share of the down contraction
+    const bool kf = d->d_model % step == 0 && d->d_ff % step == 0;
+    p.rc = bf && kf && p.nt == 1 && p.rb == 2 && d->n_shared == 0 && p.S1 >= kCutMinS1 && wsteps > kPF &&
+           p.split_ok;
+    const int upper = kind == MOE_KIND_SLOT ? 2 * kCUs : kDedupSplitUpper;
+    auto groups = [&](int t) {
+        return p.rc ? gate_up_groups_rc(t, p.S1, p.split_ok, upper) : gate_up_groups(t, p.S1, p.split_ok, upper);
+    };
+    p.g1 = groups((int)tiles);
     const bool split = p.g1 != tiles;
     // Down items in register mode: when a wave's share of the down contraction fits
     // kPF steps and one token's h fits the LDS staging budget, and the pass's work
@@ -450,12 +463,9 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
     // kernel counts its rounds on the device, over its real units (the U distinct
     // experts are not known here): its launch carries both forms of down item and the
     // grid covers the larger.
-    const int s2 = (d->d_ff + step - 1) / step;
     const int per_tok = (d->d_ff * es + 16) * (bf ? 2 : 1);  // staged bytes per token
     const int gmax = kind == MOE_KIND_SLOT ? 1 : n;  // routed group size is at most n (valid ids)
     const int64_t resident = (int64_t)kCUs * (kind == MOE_KIND_SLOT ? kResidentSlot : kResidentDedup);
-    const int wsteps = (s2 + kWaves - 1) / kWaves;  // a wave's share of the down contraction
-    const bool kf = d->d_model % step == 0 && d->d_ff % step == 0;
     // row blocks of a register-mode item: 64 rows (a wave's share at most kPF / 2
     // steps; one token tile, or two in the deduplicating kernel) or, deduplicating,
     // 32 rows of up to kPF steps for the one-token-tile variants; else 32 or 16 rows
@@ -501,7 +511,7 @@ Plan plan_for(const moe_layer_desc* d, int32_t n, int kind) {
         bool streams = false;
         for (int U = 1; U <= p.units_r; ++U) {
             const int units = U + d->n_shared;
-            const int g1 = gate_up_groups(units * p.T1, p.S1, p.split_ok, kDedupSplitUpper);
+            const int g1 = groups(units * p.T1);
             const DownShape du = down_shape(units, g1, d->d_model, reg_allowed, reg_rows, p.rb, p.reg_wgs, ks_s);
             p.grid = std::max(p.grid, g1 + units * du.T2 * du.ks);
             streams |= !du.reg;

@@ -5,7 +5,8 @@
 // (first .. last) are exactly the work groups whose shares meet the tile, in K
 // order and consecutive, at most kMaxContrib of them, so the finaliser (the last)
 // holds the highest id; cut tiles' counter indices stay below kMaxSplitTiles; and
-// the arithmetic stays below 2^31.  Prints "ok <plans checked>" or the first failure.
+// the arithmetic stays below 2^31; the same for the remainder cut (RcPlan).  Prints
+// "ok <plans checked> <remainder-cut plans checked>" or the first failure.
 #include <cstdio>
 #include <vector>
 #include "../../expert_ffn_amd/csrc/expert_kernel.h"
@@ -61,6 +62,52 @@ int main() {
                     ++plans;
                 }
             }
-    std::printf("ok %ld\n", plans);
+    // the remainder cut (kernels built with RC): whole tiles one work group each, the
+    // remainder's K steps in equal shares; same properties, cut-tile counters indexed
+    // by tile - W
+    long rc_plans = 0;
+    std::vector<int> sizes;
+    for (int t = 2 * kCUs - 8; t <= 4 * kCUs + 40; ++t) sizes.push_back(t);
+    for (int t : {896, 1792, 2688, 3584, 4480, 5376, 6272, 7168, 8192 + 77, 131072 - 5}) sizes.push_back(t);
+    for (int upper : uppers)
+        for (int S1 : {2, 3, 5, 128, 129, 448, 512})
+            for (int tiles : sizes) {
+                if (tiles < upper) continue;
+                const int g1 = gate_up_groups_rc(tiles, S1, true, upper);
+                if (g1 == tiles) {
+                    if (tiles % kCUs != 0) return fail(tiles, S1, upper, "rc: remainder left whole");
+                    continue;
+                }
+                const RcPlan rp(tiles, S1, g1);
+                if ((long)rp.Lr * rp.G2 >= (1l << 31) || (long)tiles * S1 >= (1l << 31))
+                    return fail(tiles, S1, upper, "rc: overflow");
+                if (rp.G2 < 1 || rp.G2 > kCUs) return fail(tiles, S1, upper, "rc: remainder shares");
+                const long ltot = (long)tiles * S1;
+                std::vector<int> owner((size_t)ltot, -1);
+                for (int wi = 0; wi < g1; ++wi)
+                    for (long L = rp.lbeg(wi); L < rp.lend(wi); ++L) {
+                        if (L < 0 || L >= ltot || owner[L] != -1) return fail(tiles, S1, upper, "rc: step covered twice");
+                        owner[L] = wi;
+                    }
+                for (size_t L = 0; L < owner.size(); ++L)
+                    if (owner[L] < 0) return fail(tiles, S1, upper, "rc: step not covered");
+                for (int tile = 0; tile < tiles; ++tile) {
+                    std::vector<int> meet;
+                    for (int k = 0; k < S1; ++k) {
+                        const int w = owner[(size_t)tile * S1 + k];
+                        if (meet.empty() || meet.back() != w) meet.push_back(w);
+                    }
+                    if (meet.front() != rp.first(tile) || meet.back() != rp.last(tile) ||
+                        (int)meet.size() != rp.last(tile) - rp.first(tile) + 1)
+                        return fail(tiles, S1, upper, "rc: contributors");
+                    for (size_t i = 1; i < meet.size(); ++i)
+                        if (meet[i] != meet[i - 1] + 1) return fail(tiles, S1, upper, "rc: contributors not consecutive");
+                    if ((int)meet.size() > kMaxContrib) return fail(tiles, S1, upper, "rc: too many contributors");
+                    if (meet.size() > 1 && (tile < rp.W || tile - rp.W >= kMaxSplitTiles))
+                        return fail(tiles, S1, upper, "rc: cut-tile counter out of range");
+                }
+                ++rc_plans;
+            }
+    std::printf("ok %ld %ld\n", plans, rc_plans);
     return 0;
 }

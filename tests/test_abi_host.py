@@ -343,7 +343,8 @@ def test_gate_up_split_covers_every_step_once(tmp_path):
     over tile counts 1 .. 808, K step counts 1 .. 512 and both kernels' bounds, every
     (tile, K step) is covered by exactly one work group, each cut tile's computed
     contributors are exactly the work groups meeting it (consecutive, at most
-    kMaxContrib, the finaliser last), and the arithmetic stays below 2^31."""
+    kMaxContrib, the finaliser last), and the arithmetic stays below 2^31; the same
+    for the remainder cut of large tiles (RcPlan) over tile counts up to 131067."""
     exe = str(tmp_path / "gate_up_plan_check")
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     import subprocess
