@@ -70,7 +70,7 @@ int main() {
     for (int t = 2 * kCUs - 8; t <= 4 * kCUs + 40; ++t) sizes.push_back(t);
     for (int t : {896, 1792, 2688, 3584, 4480, 5376, 6272, 7168, 8192 + 77, 131072 - 5}) sizes.push_back(t);
     for (int upper : uppers)
-        for (int S1 : {2, 3, 5, 128, 129, 448, 512})
+        for (int S1 : {2, 3, 5, 44, 64, 128, 129, 448, 512})
             for (int tiles : sizes) {
                 if (tiles < upper) continue;
                 const int g1 = gate_up_groups_rc(tiles, S1, true, upper);

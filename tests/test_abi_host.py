@@ -344,7 +344,7 @@ def test_gate_up_split_covers_every_step_once(tmp_path):
     (tile, K step) is covered by exactly one work group, each cut tile's computed
     contributors are exactly the work groups meeting it (consecutive, at most
     kMaxContrib, the finaliser last), and the arithmetic stays below 2^31; the same
-    for the remainder cut of large tiles (RcPlan) over tile counts up to 131067."""
+    for the remainder cut (RcPlan) over tile counts up to 131067 and K steps 2..512."""
     exe = str(tmp_path / "gate_up_plan_check")
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     import subprocess
