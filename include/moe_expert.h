@@ -130,9 +130,9 @@ int moe_route_group(const int32_t* ids, int32_t n, int32_t m, int32_t N, int32_t
  * parts of the d_ff contraction; P > 1 only for passes that may stream their
  * down-projection work with fewer than 4 items per compute unit) and, when the
  * pass's gate/up work may be cut between work groups (per-slot: fewer than 512
- * row tiles, or bf16 tiles of d_model >= 4096 with d_ff > 1536, whose remainder
- * beyond whole rounds of 256 tiles is cut; deduplicating: any pass, since it plans
- * for the experts it finds),
+ * row tiles, or, for bf16 passes of at most 16 tokens without shared experts,
+ * d_model >= 4096 and d_ff > 1536 (both multiples of 32), the tiles beyond whole
+ * rounds of 256; deduplicating: any pass, since it plans for the experts it finds),
  * the partial sums of tiles that work groups share (3*S*d_ff*8 bytes), each piece
  * aligned to 256 bytes.  The
  * size returned is the largest over k = 1..n, so a workspace sized for n serves
